@@ -1,0 +1,238 @@
+"""Benchmark of the Wan DiT forward on one MI355X.
+
+A step is one wan_dit_forward: one denoising step's DiT work (patch embed, time/text embedding, all
+blocks, head, unpatchify) on seeded synthetic inputs already resident in HBM.  Default workload: the
+Wan2.1-T2V-1.3B geometry with the CFG pair as batch 2 (2 x 32760 tokens, 30 blocks, bf16).
+
+Prints one JSON line.  `value` is the achieved throughput in TFLOP/s of algorithmic work (GEMM and
+attention FLOPs) per step; `ms_per_step` the mean step time.  `roofline` reports the dominant kernel
+(self-attention) timed with HIP events around its own launches on the stream it runs on, and
+`cpu_baseline` the fp64 oracle on a bounded sample of the same workload, scaled to a full step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def step_flops(cfg, B=None, L=None) -> dict:
+    """Algorithmic FLOPs of one forward: 2*M*N*K per GEMM, 4*B*Lq*Lkv*D per attention."""
+    B = B or cfg.batch
+    L = L or cfg.tokens
+    D, Fd, Lt, N = cfg.dim, cfg.ffn_dim, cfg.text_len, cfg.num_layers
+    M = B * L
+    R = M if cfg.per_token_t else B
+    f = {}
+    f["patch_embed"] = 2 * M * cfg.patch_k * D
+    f["time_mlp_fp32"] = 2 * R * (cfg.freq_dim * D + D * D + 6 * D * D)
+    f["text_proj"] = 2 * B * Lt * (cfg.text_dim * D + D * D)
+    per_block = {
+        "qkv": 2 * M * D * 3 * D, "o": 2 * M * D * D, "q2": 2 * M * D * D, "kv2": 2 * B * Lt * D * 2 * D,
+        "o2": 2 * M * D * D, "ffn": 2 * 2 * M * D * Fd, "self_attn": 4 * B * L * L * D, "cross_attn": 4 * B * L * Lt * D,
+    }
+    for k, v in per_block.items():
+        f[k] = v * N
+    f["proj_out"] = 2 * M * D * cfg.out_k
+    f["total"] = sum(f.values())
+    return f
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "video_diffusion_transformer_patchify_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_file: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if recorded for the current source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(kernel_file)
+    if not rec or rec.get("source_hash") != source_hash(kernel_file, "common.h"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_self_attention(B, cfg, reps, stream):
+    """Average duration of the self-attention kernel at the workload's shape, HIP events on its stream."""
+    import torch
+
+    from video_diffusion_transformer_patchify_amd import binding as Bd
+
+    D, nh, L = cfg.dim, cfg.num_heads, cfg.tokens
+    g = torch.Generator(device="cuda").manual_seed(0)
+    qkv = (torch.randn((B * L, 3 * D), generator=g, device="cuda") * 1.0).to(torch.bfloat16)
+    ldv = (L + 63) // 64 * 64
+    vt = Bd.op_transpose_v(qkv, 2 * D, B, L, nh, ldv, stream=stream)
+    out = torch.empty((B * L, D), dtype=torch.bfloat16, device="cuda")
+    for _ in range(2):
+        Bd.op_attention(qkv, qkv[:, D:], vt, out, B, L, L, nh, stream=stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        Bd.op_attention(qkv, qkv[:, D:], vt, out, B, L, L, nh, stream=stream)
+    ev1.record(stream)
+    ev1.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    del qkv, vt, out
+    return ms
+
+
+def cpu_baseline(cfg, budget_s: float):
+    """fp64 oracle on a bounded sample: one transformer block for one batch element of the workload,
+    with the self-attention restricted to a sample of query rows; scaled to one full step."""
+    import numpy as np
+
+    from oracle import wan_oracle as O
+    from wan_inputs import Weights
+
+    threads = len(os.sched_getaffinity(0))
+    one = cfg.replace(batch=1, num_layers=1)
+    w = Weights(one)
+    rng = np.random.default_rng(0)
+    L, D, nh = one.tokens, one.dim, one.num_heads
+    x = rng.standard_normal((1, L, D))
+    ctx = rng.standard_normal((1, one.text_len, D))
+    tproj = rng.standard_normal((1, 6, D)) * 0.1
+    ang = O.rope_angles(one.post_f, one.post_h, one.post_w)
+    for n in w.names():
+        w.f64(n)
+    p = "blocks.0."
+    # Untimed: q/k/v of all L tokens, so the self-attention sample sees every key.
+    y = O.layer_norm(x, one.eps)
+    q = O.rms_norm(O.linear(y, w.f64(p + "attn1.to_q.weight"), w.f64(p + "attn1.to_q.bias")), one.eps)
+    k = O.rms_norm(O.linear(y, w.f64(p + "attn1.to_k.weight"), w.f64(p + "attn1.to_k.bias")), one.eps)
+    v = O.linear(y, w.f64(p + "attn1.to_v.weight"), w.f64(p + "attn1.to_v.bias"))
+    nq = 256
+    qh = O.apply_rope(q[0].reshape(L, nh, 128), ang)[:nq]
+    kh = O.apply_rope(k[0].reshape(L, nh, 128), ang)
+    vh = v[0].reshape(L, nh, 128)
+    del y, q, k, v
+    # Timed sample: self-attention of nq query rows per head against all L keys, plus one whole block
+    # (projections, cross-attention, FFN, norms) on nq tokens; both scale linearly to L tokens.
+    t1 = time.perf_counter()
+    O.attention(qh, kh, vh, workers=threads)
+    t_attn = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    O.block_forward(x[:, :nq], ctx, tproj, ang[:nq], w, p, nh, one.eps)
+    t_rest = time.perf_counter() - t2
+    est_block = (t_attn + t_rest) * (L / nq)
+    est_step = est_block * cfg.batch * cfg.num_layers
+    sample_s = t_attn + t_rest
+    return est_step, sample_s, threads, nq
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Wan2.1-1.3B, 2x32760 tokens")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from video_diffusion_transformer_patchify_amd import binding as Bd
+    from video_diffusion_transformer_patchify_amd.harness import to_device, upload_weights
+    from wan_inputs import Weights, draw_inputs, get_config
+
+    cfg = get_config(args.config)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    t_setup = time.perf_counter()
+    w = Weights(cfg)
+    model = Bd.WanDiT(Bd.make_config(cfg), upload_weights(w, drop=True), stream=stream)
+    torch.cuda.empty_cache()
+    lat, t, txt = draw_inputs(cfg)
+    latent, ts, text = to_device(lat), to_device(t), to_device(txt)
+    out = torch.empty(cfg.out_shape, dtype=latent.dtype, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    print(f"# setup {setup_s:.1f}s, device bytes {model.device_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        model.forward(latent, ts, text, out, stream=stream)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        model.forward(latent, ts, text, out, stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"# timed {args.steps} steps: {ms:.2f} ms/step (wall {wall * 1e3 / args.steps:.2f})", file=sys.stderr, flush=True)
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    fl = step_flops(cfg)
+    tflops = fl["total"] / (ms * 1e-3) / 1e12
+
+    # dominant kernel: self-attention, timed on the stream it is launched on
+    attn_ms = time_self_attention(cfg.batch, cfg, 10, stream)
+    attn_flops = 4 * cfg.batch * cfg.tokens * cfg.tokens * cfg.dim
+    attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
+    print(f"# self-attention kernel {attn_ms:.3f} ms/launch = {attn_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    model.close()
+    del latent, text, out
+    torch.cuda.empty_cache()
+
+    res = {
+        "metric": "DiT fwd ms/step + MFMA TFLOP/s, Wan-1.3B geometry, 32760 tokens bf16",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latent/text, N(0,0.02) random-init weights)",
+        "config": {"workload": f"{cfg.name}: B={cfg.batch}, latent {list(cfg.latent_shape)}, {cfg.tokens} tokens/sample, "
+                               f"D={cfg.dim}, {cfg.num_heads} heads, FFN {cfg.ffn_dim}, {cfg.num_layers} blocks, "
+                               f"text {cfg.text_len}x{cfg.text_dim}",
+                   "global_batch": cfg.batch, "seq_len": cfg.tokens, "parallelism": "single GPU"},
+        "mfma_frac_end_to_end": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": fl["total"],
+        "roofline": {"kernel": "k_flash_attn<self> (self-attention)", "bound": "mfma", "achieved": round(attn_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+                     "ms_per_launch": round(attn_ms, 3), "flops_per_launch": attn_flops,
+                     "traffic": traffic_for("k_attn.hip")},
+    }
+    if not args.no_cpu_baseline:
+        est_step, sample_s, threads, nq = cpu_baseline(cfg, args.cpu_budget)
+        res["cpu_baseline"] = {
+            "value": round(fl["total"] / est_step / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "ms_per_step": round(est_step * 1e3, 1),
+            "sample": f"fp64 numpy oracle: one block for one batch element ({cfg.tokens} tokens) with self-attention "
+                      f"on {nq} query rows per head against all keys plus the rest of the block on {nq} tokens, "
+                      f"{sample_s:.1f}s measured, scaled x{cfg.tokens}/{nq} (tokens) x{cfg.batch} (batch) "
+                      f"x{cfg.num_layers} (blocks)",
+        }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

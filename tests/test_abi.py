@@ -1,0 +1,73 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad arguments before touching the GPU.
+
+CPU-only: no call here reaches a kernel launch (every call fails validation first).
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "video_diffusion_transformer_patchify_amd", "libwan_dit.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libwan_dit.so not built")
+
+
+def declared_functions():
+    names = []
+    for h in ("wan_dit.h", "wan_ops.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(wan_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = C.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_lists_every_declared_symbol():
+    from video_diffusion_transformer_patchify_amd import binding
+
+    assert sorted(binding.EXPORTED) == declared_functions()
+
+
+def test_validation_errors_without_gpu():
+    from video_diffusion_transformer_patchify_amd import binding as B
+
+    # create: NULL config / NULL out
+    h = C.c_void_p()
+    assert B._create(None, None, 0, None, C.byref(h)) == 1
+    assert "config" in B.last_error()
+    cfg = B.WanDitConfig()
+    assert B._create(C.byref(cfg), None, 0, None, None) == 1
+    # unsupported head_dim
+    from wan_inputs import get_config
+
+    c = B.make_config(get_config(1))
+    c.head_dim = 64
+    assert B._create(C.byref(c), None, 0, None, C.byref(h)) == 4
+    assert "head_dim" in B.last_error()
+    c = B.make_config(get_config(1))
+    c.patch_h = 4
+    assert B._create(C.byref(c), None, 0, None, C.byref(h)) == 4
+    # missing weights are reported by name
+    c = B.make_config(get_config(1))
+    assert B._create(C.byref(c), None, 0, None, C.byref(h)) == 7
+    assert "patch_embedding.weight" in B.last_error()
+    # forward on a NULL handle
+    assert B._forward(None, None, None, None, None, None) == 1
+    # op argument checks
+    assert B._op_gemm(1, 64, 1, 64, 1, 10, 64, 60, 0, 1, 64, None, None, 0, 1, None) == 2      # K % 64
+    assert B._op_gemm(1, 64, 1, 64, 1, 10, 64, 64, 9, 1, 64, None, None, 0, 1, None) == 1      # epilogue
+    assert B._op_gemm(1, 64, 1, 64, 1, 10, 64, 64, 4, 1, 64, None, None, 0, 1, None) == 1      # gate missing
+    assert B._op_patchify(1, 0, 1, 16, 5, 15, 16, 64, 1, None) == 2                             # odd height
+    assert B._op_attention(1, 1536, 1, 1536, 1, 100, 1, 1536, 1, 320, 320, 12, None) == 2       # ldv < Lkv
+    assert B._op_layernorm(1, 4, 1000, 1e-6, 0, 1, 1, 1, 0, 0, 0, 1, None, None, 1, None) == 2  # D % 256
+    assert B._op_qk_norm_rope(1, 4608, 4, 1536, 1e-6, 0, 1, 1536, 1, 1, 10, 2, 2, 2, 44, 42, 42, None) == 2
+    assert B._op_rope_table(1, 5, 8, 8, 44, 42, 40, 1e4, None) == 2                              # dims sum != 128

@@ -1,0 +1,356 @@
+"""Per-stage parity of the HIP kernels against the fp64 oracle, called through the C ABI.
+
+Index kernels (patchify, unpatchify, V transpose) must match bit for bit.  Arithmetic kernels get
+per-stage budgets derived from their last rounding step: a bf16 output carries at most 2^-9 relative
+rounding error per element (rel-L2 about 1.1e-3 for random data), fp32 outputs only accumulation
+error.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import wan_oracle as O
+from wan_inputs import f32_to_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def G():
+    import gpu_common  # raises if the HIP library is missing: no fallback
+
+    return gpu_common
+
+
+def _round_up(a, b):
+    return (a + b - 1) // b * b
+
+
+# ------------------------------------------------------------------------------------------------
+# patchify / unpatchify / V transpose: bit-exact
+# ------------------------------------------------------------------------------------------------
+
+PATCH_SHAPES = [
+    ((1, 16, 5, 16, 16), "f32"),        # tiny reference (fp32 latent)
+    ((2, 3, 3, 6, 10), "bf16"),         # ragged, kp padding
+    ((2, 16, 21, 60, 104), "bf16"),     # Wan2.1 1.3B, CFG batch 2
+    ((1, 36, 9, 44, 80), "bf16"),       # I2V stack
+    ((1, 48, 31, 44, 80), "bf16"),      # TI2V-5B
+    ((1, 16, 21, 90, 160), "bf16"),     # 14B 720p
+]
+
+
+@pytest.mark.parametrize("shape,dt", PATCH_SHAPES)
+def test_patchify_bitexact(G, shape, dt):
+    G.note(f"patchify {shape} {dt}")
+    t = G.draw_normal(9, f"patch{shape}", shape, dt)
+    x = G.to_device(t)
+    kp = _round_up(4 * shape[1], 64)
+    p = G.B.op_patchify(x, kp)
+    G.sync()
+    got = G.bf16_bits(p)
+    ref = O.patchify(t.f32())                      # exact copy of the stored values, float32
+    want = np.zeros((ref.shape[0] * ref.shape[1], kp), dtype=np.uint16)
+    want[:, : ref.shape[2]] = f32_to_bf16_bits(ref.reshape(-1, ref.shape[2])).reshape(-1, ref.shape[2])
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 5, 16, 16), (2, 3, 3, 6, 10), (2, 16, 21, 60, 104), (1, 48, 31, 44, 80)])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_unpatchify_bitexact(G, shape, out_dt):
+    import torch
+
+    G.note(f"unpatchify {shape} {out_dt}")
+    b, c, f, hz, wz = shape
+    L = f * (hz // 2) * (wz // 2)
+    ldz = 4 * c + 4                                  # a padded row stride
+    zt = G.draw_normal(9, f"z{shape}", (b * L, ldz), "f32")
+    z = G.to_device(zt)
+    out = G.B.op_unpatchify(z, b, c, f, hz, wz, torch.float32 if out_dt == "f32" else torch.bfloat16)
+    G.sync()
+    ref = O.unpatchify(zt.f32()[:, : 4 * c].reshape(b, L, 4 * c), f, hz, wz, c)
+    if out_dt == "f32":
+        assert np.array_equal(out.cpu().numpy(), ref)
+    else:
+        assert np.array_equal(G.bf16_bits(out), f32_to_bf16_bits(ref).reshape(ref.shape))
+
+
+@pytest.mark.parametrize("B,L,nh,col_off,ld", [(2, 320, 12, 3072, 4608), (1, 1000, 3, 384, 768), (2, 226, 12, 1536, 3072),
+                                               (2, 32760, 12, 3072, 4608)])
+def test_transpose_v_bitexact(G, B, L, nh, col_off, ld):
+    G.note(f"transpose_v B={B} L={L} nh={nh}")
+    src, _ = G.bf16_dev((B * L, ld), f"tv{L}")
+    ldv = _round_up(L, 64)
+    vt = G.B.op_transpose_v(src, col_off, B, L, nh, ldv)
+    G.sync()
+    s = G.bf16_bits(src)
+    want = np.zeros((B, nh, 128, ldv), dtype=np.uint16)
+    want[:, :, :, :L] = s.reshape(B, L, ld)[:, :, col_off:col_off + 128 * nh].reshape(B, L, nh, 128).transpose(0, 2, 3, 1)
+    assert np.array_equal(G.bf16_bits(vt), want)
+
+
+# ------------------------------------------------------------------------------------------------
+# GEMM + epilogues
+# ------------------------------------------------------------------------------------------------
+
+GEMM_CASES = [(1, 64, 64), (300, 192, 64), (4133, 1536, 1536), (452, 3072, 1536), (1000, 8960, 1536),
+              (777, 1536, 8960), (65520, 1536, 1536)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
+def test_gemm_epilogues(G, M, N, K, epi):
+    import torch
+
+    if M * N > 5e7 and epi not in (0, 4):
+        pytest.skip("full-size shape checked with the bf16 and gated epilogues")
+    G.note(f"gemm M={M} N={N} K={K} epi={epi}")
+    x, xh = G.bf16_dev((M, K), f"gx{M}{K}")
+    w, wh = G.bf16_dev((N, K), f"gw{N}{K}", 0.02)
+    bt = G.draw_normal(0, f"gb{N}", (N,), "f32", 0.02)
+    bias, bh = G.to_device(bt), bt.f64()
+    rows = np.arange(M) if M <= 5000 else np.unique(np.concatenate([np.arange(64), np.arange(M - 200, M),
+                                                                     np.random.default_rng(0).integers(0, M, 300)]))
+    lin = xh[rows] @ wh.T + bh                     # oracle: nn.Linear in float64
+    if epi in (0, 1):
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        G.B.op_gemm(x, w, bias, epi, out)
+        G.sync()
+        got = G.to_f64(out)[rows]
+        ref = O.gelu_tanh(lin) if epi == 1 else lin
+        # one bf16 rounding of the fp32 result
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+        assert G.rel_l2(got, ref) < 3e-3
+        return
+    x0t = G.draw_normal(0, f"gx0{M}{N}", (M, N), "f32")
+    out = G.to_device(x0t).clone()
+    x0 = x0t.f64()[rows]
+    if epi == 2:
+        G.B.op_gemm(x, w, bias, epi, out)
+        ref = lin
+    elif epi == 3:
+        G.B.op_gemm(x, w, bias, epi, out)
+        ref = x0 + lin
+    else:
+        L = 100 if M > 100 else 1                 # tokens per gate row
+        nsrc = (M + L - 1) // L
+        tab_t = G.draw_normal(0, "gtab", (N,), "f32", 0.5)
+        src_t = G.draw_normal(0, f"gsrc{nsrc}", (nsrc, 6 * N), "f32", 0.5)
+        src = G.to_device(src_t)
+        G.B.op_gemm(x, w, bias, epi, out, gate_tab=G.to_device(tab_t), gate_src=src[:, 2 * N:], gate_ld=6 * N,
+                    rows_per_gate=L)
+        gate = tab_t.f64()[None, :] + src_t.f64()[rows // L, 2 * N:3 * N]
+        ref = x0 + lin * gate
+    G.sync()
+    got = G.to_f64(out)[rows]
+    assert G.rel_l2(got - x0 if epi != 2 else got, ref - x0 if epi != 2 else ref) < 1e-5
+    assert G.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max())
+
+
+# ------------------------------------------------------------------------------------------------
+# LayerNorm + modulation
+# ------------------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("rows,D", [(300, 1536), (1000, 3072), (77, 5120), (65520, 1536)])
+@pytest.mark.parametrize("mode", ["sample", "token", "affine", "head"])
+def test_layernorm(G, rows, D, mode):
+    import torch
+
+    G.note(f"layernorm rows={rows} D={D} mode={mode}")
+    xt = G.draw_normal(1, f"lnx{rows}{D}", (rows, D), "f32", 2.0)
+    xh = xt.f64() + 0.75                          # non-zero mean
+    x = torch.from_numpy(xh.astype(np.float32)).cuda()
+    xh = xh.astype(np.float32).astype(np.float64)
+    y = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+    eps = 1e-6
+    ln = O.layer_norm(xh, eps)
+    if mode == "affine":
+        g_t = G.draw_uniform(1, "lng", (D,), 0.5, 1.5)
+        b_t = G.draw_normal(1, "lnb", (D,), "f32", 0.02)
+        G.B.op_layernorm(x, eps, 1, y, gamma=G.to_device(g_t), beta=G.to_device(b_t))
+        ref = ln * g_t.f64() + b_t.f64()
+    else:
+        nsl = 6 if mode != "head" else 1
+        tab_t = G.draw_normal(1, "lntab", (nsl if mode != "head" else 2, D), "f32", 1.0 / math.sqrt(D))
+        L = 1 if mode == "token" else 100
+        nsrc = (rows + L - 1) // L
+        src_t = G.draw_normal(1, f"lnsrc{nsrc}{D}", (nsrc, nsl * D), "f32", 0.3)
+        tab, src = G.to_device(tab_t), G.to_device(src_t)
+        if mode == "head":
+            G.B.op_layernorm(x, eps, 0, y, tab_shift=tab[0], tab_scale=tab[1], src=src, src_ld=D, src_shift_off=0,
+                             src_scale_off=0, rows_per_src=L)
+            s = src_t.f64()[np.arange(rows) // L]
+            shift, scale = tab_t.f64()[0] + s, tab_t.f64()[1] + s
+        else:
+            G.B.op_layernorm(x, eps, 0, y, tab_shift=tab[3], tab_scale=tab[4], src=src, src_ld=6 * D,
+                             src_shift_off=3 * D, src_scale_off=4 * D, rows_per_src=L)
+            s = src_t.f64()[np.arange(rows) // L]
+            shift, scale = tab_t.f64()[3] + s[:, 3 * D:4 * D], tab_t.f64()[4] + s[:, 4 * D:5 * D]
+        ref = ln * (1.0 + scale) + shift
+    G.sync()
+    got = G.to_f64(y)
+    assert G.rel_l2(got, ref) < 3e-3
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max())
+
+
+# ------------------------------------------------------------------------------------------------
+# QK RMSNorm + 3D RoPE
+# ------------------------------------------------------------------------------------------------
+
+
+def test_rope_table(G):
+    G.note("rope table")
+    fp, hp, wp = 21, 30, 52
+    tab = G.B.op_rope_table(fp, hp, wp).cpu().numpy().astype(np.float64)
+    ang = O.rope_angles(fp, hp, wp)
+    n = fp * 22 + hp * 21 + wp * 21
+    cos, sin = tab[:n], tab[n:]
+    # rebuild the per-token angle table from the per-axis rows and compare with the oracle
+    f_idx, h_idx, w_idx = np.meshgrid(np.arange(fp), np.arange(hp), np.arange(wp), indexing="ij")
+    f_idx, h_idx, w_idx = f_idx.ravel(), h_idx.ravel(), w_idx.ravel()
+    ct = cos[: fp * 22].reshape(fp, 22)
+    ch = cos[fp * 22: fp * 22 + hp * 21].reshape(hp, 21)
+    cw = cos[fp * 22 + hp * 21:].reshape(wp, 21)
+    st = sin[: fp * 22].reshape(fp, 22)
+    sh = sin[fp * 22: fp * 22 + hp * 21].reshape(hp, 21)
+    sw = sin[fp * 22 + hp * 21:].reshape(wp, 21)
+    c_all = np.concatenate([ct[f_idx], ch[h_idx], cw[w_idx]], axis=1)
+    s_all = np.concatenate([st[f_idx], sh[h_idx], sw[w_idx]], axis=1)
+    assert np.abs(c_all - np.cos(ang)).max() < 1e-7 and np.abs(s_all - np.sin(ang)).max() < 1e-7
+
+
+@pytest.mark.parametrize("B,grid,D", [(1, (5, 8, 8), 1536), (2, (3, 6, 10), 3072), (1, (9, 22, 40), 5120),
+                                      (2, (21, 30, 52), 1536)])
+def test_qk_norm_rope(G, B, grid, D):
+    G.note(f"qk_norm_rope B={B} grid={grid} D={D}")
+    fp, hp, wp = grid
+    L = fp * hp * wp
+    rows = B * L
+    buf, bh = G.bf16_dev((rows, 3 * D), f"qkb{rows}{D}", 0.05)
+    gq_t, gk_t = G.draw_uniform(2, "gq", (D,), 0.5, 1.5), G.draw_uniform(2, "gk", (D,), 0.5, 1.5)
+    v_before = G.bf16_bits(buf)[:, 2 * D:].copy()
+    tab = G.B.op_rope_table(fp, hp, wp)
+    G.B.op_qk_norm_rope(buf, D, 1e-6, 0, G.to_device(gq_t), D, G.to_device(gk_t), tab, L, grid)
+    G.sync()
+    out_bits = G.bf16_bits(buf)
+    assert np.array_equal(out_bits[:, 2 * D:], v_before)        # V untouched
+    got = G.to_f64(buf)
+    sel = np.arange(rows) if rows <= 20000 else np.unique(np.random.default_rng(1).integers(0, rows, 2000))
+    ang = O.rope_angles(fp, hp, wp)
+    for seg, g_t in ((0, gq_t), (1, gk_t)):
+        u = O.rms_norm(bh[sel, seg * D:(seg + 1) * D], 1e-6, g_t.f64())
+        # rotate row by row with the oracle (each row has its own token position)
+        ref = np.empty_like(u)
+        for i in range(len(sel)):
+            ref[i] = O.apply_rope(u[i].reshape(1, D // 128, 128), ang[[sel[i] % L]]).reshape(D)
+        g = got[sel, seg * D:(seg + 1) * D]
+        assert G.rel_l2(g, ref) < 3e-3
+        assert np.all(np.abs(g - ref) <= 2.0 ** -8 * np.abs(ref) + 2e-3 * np.abs(ref).max())
+
+
+def test_rms_norm_single_segment(G):
+    G.note("rms single segment")
+    D, rows = 5120, 1024
+    buf, bh = G.bf16_dev((rows, 2 * D), "rms1", 0.05)
+    g_t = G.draw_uniform(2, "g2", (D,), 0.5, 1.5)
+    keep = G.bf16_bits(buf)[:, D:].copy()
+    G.B.op_qk_norm_rope(buf, D, 1e-6, 0, G.to_device(g_t))
+    G.sync()
+    assert np.array_equal(G.bf16_bits(buf)[:, D:], keep)
+    ref = O.rms_norm(bh[:, :D], 1e-6, g_t.f64())
+    assert G.rel_l2(G.to_f64(buf)[:, :D], ref) < 3e-3
+
+
+# ------------------------------------------------------------------------------------------------
+# attention
+# ------------------------------------------------------------------------------------------------
+
+
+def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None):
+    import torch
+
+    D = 128 * nh
+    if fused:                                     # self-attention layout: q | k | v in one [B*L, 3D] buffer
+        assert Lq == Lkv
+        qkv, qh = G.bf16_dev((B * Lq, 3 * D), name, scale)
+        q, k = qkv, qkv[:, D:]
+        kh = qh[:, D:2 * D]
+        vh = qh[:, 2 * D:]
+        qh = qh[:, :D]
+        vt = G.B.op_transpose_v(qkv, 2 * D, B, Lkv, nh, _round_up(Lkv, 64))
+    else:                                         # cross layout: q [B*Lq, D], kv [B*Lkv, 2D]
+        q, qh = G.bf16_dev((B * Lq, D), name + "q", scale)
+        kv, kvh = G.bf16_dev((B * Lkv, 2 * D), name + "kv", scale)
+        k = kv
+        kh, vh = kvh[:, :D], kvh[:, D:]
+        vt = G.B.op_transpose_v(kv, D, B, Lkv, nh, _round_up(Lkv, 64))
+    out = torch.empty((B * Lq, D), dtype=torch.bfloat16, device="cuda")
+    G.B.op_attention(q, k, vt, out, B, Lq, Lkv, nh)
+    G.sync()
+    got = G.to_f64(out)
+    for b in range(B):
+        sel = np.arange(Lq) if rows is None else rows
+        qb = qh[b * Lq:(b + 1) * Lq][sel].reshape(len(sel), nh, 128)
+        kb = kh[b * Lkv:(b + 1) * Lkv].reshape(Lkv, nh, 128)
+        vb = vh[b * Lkv:(b + 1) * Lkv].reshape(Lkv, nh, 128)
+        ref = O.attention(qb, kb, vb, workers=4).reshape(len(sel), D)
+        g = got[b * Lq:(b + 1) * Lq][sel]
+        assert G.rel_l2(g, ref) < 6e-3, (b, G.rel_l2(g, ref))
+        assert G.max_abs(g, ref) < 2e-2 * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("B,L,nh", [(1, 320, 12), (2, 1000, 3), (1, 64, 2), (1, 1, 1), (2, 129, 4), (1, 7920, 2)])
+def test_self_attention(G, B, L, nh):
+    G.note(f"self attention B={B} L={L} nh={nh}")
+    _attn_case(G, B, L, L, nh, True, f"sa{B}_{L}_{nh}")
+
+
+@pytest.mark.parametrize("B,Lq,Lkv,nh", [(2, 320, 226, 12), (1, 1000, 512, 4), (2, 77, 1, 2), (1, 200, 64, 3)])
+def test_cross_attention(G, B, Lq, Lkv, nh):
+    G.note(f"cross attention B={B} Lq={Lq} Lkv={Lkv} nh={nh}")
+    _attn_case(G, B, Lq, Lkv, nh, False, f"ca{B}_{Lq}_{Lkv}_{nh}")
+
+
+def test_attention_peaked_scores(G):
+    """Large-magnitude q/k (scores in the tens): exercises the running max and rescaling."""
+    G.note("attention peaked")
+    _attn_case(G, 1, 500, 500, 2, True, "peaked", scale=3.0)
+
+
+def test_self_attention_full_size_sampled(G):
+    """Wan2.1-1.3B geometry: B=2, 12 heads, 32760 tokens; sampled query rows against the oracle."""
+    G.note("self attention full size B=2 L=32760 nh=12")
+    rows = np.unique(np.concatenate([np.arange(3), [32700, 32759], np.random.default_rng(3).integers(0, 32760, 8)]))
+    _attn_case(G, 2, 32760, 32760, 12, True, "safull", rows=rows)
+
+
+# ------------------------------------------------------------------------------------------------
+# timestep embedding (fp32)
+# ------------------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("rows,D,per_token", [(2, 1536, False), (1, 5120, False), (2000, 3072, True)])
+def test_time_embed(G, rows, D, per_token):
+    import torch
+
+    G.note(f"time embed rows={rows} D={D}")
+    if per_token:
+        t_t = G.draw_uniform(3, "tt", (rows,), 0.0, 999.9)
+    else:
+        t_t = None
+    t_h = t_t.f64() if per_token else np.full(rows, 500.0)
+    t = G.to_device(t_t) if per_token else torch.full((rows,), 500.0, device="cuda")
+    ws = {}
+    for n, shp in (("w1", (D, 256)), ("b1", (D,)), ("w2", (D, D)), ("b2", (D,)), ("wp", (6 * D, D)), ("bp", (6 * D,))):
+        ws[n] = G.draw_normal(3, f"te{n}{D}", shp, "f32", 0.02)
+    dev = {n: G.to_device(v) for n, v in ws.items()}
+    temb, tproj = G.B.op_time_embed(t, 256, D, dev["w1"], dev["b1"], dev["w2"], dev["b2"], dev["wp"], dev["bp"])
+    G.sync()
+    w = {"time_embedder.linear_1.weight": ws["w1"].f64(), "time_embedder.linear_1.bias": ws["b1"].f64(),
+         "time_embedder.linear_2.weight": ws["w2"].f64(), "time_embedder.linear_2.bias": ws["b2"].f64(),
+         "time_proj.weight": ws["wp"].f64(), "time_proj.bias": ws["bp"].f64()}
+    r_temb, r_tproj = O.time_embed(t_h, w)
+    assert G.rel_l2(G.to_f64(temb), r_temb) < 1e-4
+    assert G.rel_l2(G.to_f64(tproj), r_tproj.reshape(rows, 6 * D)) < 1e-4

@@ -1,0 +1,269 @@
+"""ctypes binding of libwan_dit.so (include/wan_dit.h, include/wan_ops.h).
+
+Argument marshalling only: every stage runs in the HIP library.  torch provides device memory and the
+current stream.  If the library has not been built this module raises at import time; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwan_dit.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m video_diffusion_transformer_patchify_amd.build`")
+lib = C.CDLL(_LIB_PATH)
+
+WAN_F32, WAN_BF16 = 0, 1
+EPI_BF16, EPI_GELU_BF16, EPI_F32, EPI_RES_F32, EPI_GATE_F32 = range(5)
+STATUS = {0: "WAN_OK", 1: "WAN_ERR_INVALID_ARG", 2: "WAN_ERR_SHAPE", 3: "WAN_ERR_DTYPE", 4: "WAN_ERR_UNSUPPORTED",
+          5: "WAN_ERR_OOM", 6: "WAN_ERR_HIP", 7: "WAN_ERR_MISSING_WEIGHT"}
+
+
+class WanError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class WanTensor(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int32), ("ndim", C.c_int32), ("shape", C.c_int64 * 6)]
+
+
+class WanWeight(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("data", C.c_void_p), ("dtype", C.c_int32), ("ndim", C.c_int32),
+                ("shape", C.c_int64 * 6)]
+
+
+class WanDitConfig(C.Structure):
+    _fields_ = [("dim", C.c_int32), ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn_dim", C.c_int32),
+                ("num_layers", C.c_int32), ("in_channels", C.c_int32), ("out_channels", C.c_int32),
+                ("text_dim", C.c_int32), ("freq_dim", C.c_int32), ("patch_t", C.c_int32), ("patch_h", C.c_int32),
+                ("patch_w", C.c_int32), ("rope_dim_t", C.c_int32), ("rope_dim_h", C.c_int32),
+                ("rope_dim_w", C.c_int32), ("per_token_timestep", C.c_int32), ("eps", C.c_float),
+                ("reserved0", C.c_float), ("rope_theta", C.c_double), ("max_batch", C.c_int64),
+                ("max_tokens", C.c_int64), ("max_text_len", C.c_int64)]
+
+
+_vp, _i64, _i32, _f32, _f64 = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_double
+
+
+def _sig(name, args, res=C.c_int):
+    f = getattr(lib, name)
+    f.argtypes = args
+    f.restype = res
+    return f
+
+
+_create = _sig("wan_dit_create", [C.POINTER(WanDitConfig), C.POINTER(WanWeight), C.c_size_t, _vp, C.POINTER(_vp)])
+_forward = _sig("wan_dit_forward", [_vp, C.POINTER(WanTensor), C.POINTER(WanTensor), C.POINTER(WanTensor),
+                                    C.POINTER(WanTensor), _vp])
+_destroy = _sig("wan_dit_destroy", [_vp], None)
+_last_error = _sig("wan_dit_last_error", [], C.c_char_p)
+_device_bytes = _sig("wan_dit_device_bytes", [_vp], _i64)
+_op_patchify = _sig("wan_op_patchify", [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp])
+_op_unpatchify = _sig("wan_op_unpatchify", [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp])
+_op_gemm = _sig("wan_op_gemm", [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
+                                _vp])
+_op_layernorm = _sig("wan_op_layernorm", [_vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp,
+                                          _vp, _vp, _vp])
+_op_rope_table_floats = _sig("wan_op_rope_table_floats", [_i32] * 6, _i64)
+_op_rope_table = _sig("wan_op_rope_table", [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _f64, _vp])
+_op_qk_norm_rope = _sig("wan_op_qk_norm_rope", [_vp, _i64, _i64, _i64, _f32, _i64, _vp, _i64, _vp, _vp, _i64, _i32,
+                                                _i32, _i32, _i32, _i32, _i32, _vp])
+_op_transpose_v = _sig("wan_op_transpose_v", [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp])
+_op_attention = _sig("wan_op_attention", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp])
+_op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
+
+EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
+            "wan_op_patchify", "wan_op_unpatchify", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
+            "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
+            "wan_op_time_embed"]
+
+
+def last_error() -> str:
+    return (_last_error() or b"").decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise WanError(status, last_error())
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return WAN_F32
+    if t.dtype == torch.bfloat16:
+        return WAN_BF16
+    raise WanError(3, f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def as_wan_tensor(t: torch.Tensor) -> WanTensor:
+    if not t.is_contiguous():
+        raise WanError(1, "tensors passed to the library must be contiguous")
+    w = WanTensor()
+    w.data = t.data_ptr()
+    w.dtype = _dtype_code(t)
+    w.ndim = t.dim()
+    for i, s in enumerate(t.shape):
+        w.shape[i] = s
+    return w
+
+
+def make_config(cfg, max_batch=None, max_tokens=None, max_text_len=None, num_layers=None) -> WanDitConfig:
+    """Fill the C config from a geometry object with the wan_inputs.WanConfig attributes."""
+    c = WanDitConfig()
+    c.dim, c.num_heads, c.head_dim, c.ffn_dim = cfg.dim, cfg.num_heads, cfg.head_dim, cfg.ffn_dim
+    c.num_layers = cfg.num_layers if num_layers is None else num_layers
+    c.in_channels, c.out_channels, c.text_dim, c.freq_dim = cfg.in_channels, cfg.out_channels, cfg.text_dim, cfg.freq_dim
+    c.patch_t, c.patch_h, c.patch_w = cfg.patch
+    c.rope_dim_t, c.rope_dim_h, c.rope_dim_w = cfg.rope_dims
+    c.per_token_timestep = 1 if cfg.per_token_t else 0
+    c.eps = cfg.eps
+    c.rope_theta = cfg.rope_theta
+    c.max_batch = max_batch or cfg.batch
+    c.max_tokens = max_tokens or cfg.tokens
+    c.max_text_len = max_text_len or cfg.text_len
+    return c
+
+
+class WanDiT:
+    """Handle around wan_dit_create / wan_dit_forward / wan_dit_destroy."""
+
+    def __init__(self, config: WanDitConfig, weights: dict, stream=None):
+        names = list(weights)
+        arr = (WanWeight * len(names))()
+        self._keep = []
+        for i, n in enumerate(names):
+            t = weights[n]
+            if not t.is_cuda or not t.is_contiguous():
+                raise WanError(1, f"weight {n} must be a contiguous device tensor")
+            b = n.encode()
+            self._keep.append(b)
+            arr[i].name = b
+            arr[i].data = t.data_ptr()
+            arr[i].dtype = _dtype_code(t)
+            arr[i].ndim = t.dim()
+            for j, s in enumerate(t.shape):
+                arr[i].shape[j] = s
+        self.config = config
+        h = C.c_void_p()
+        _check(_create(C.byref(config), arr, len(names), _stream(stream), C.byref(h)))
+        self._h = h
+
+    @property
+    def device_bytes(self) -> int:
+        return int(_device_bytes(self._h))
+
+    def forward(self, latent: torch.Tensor, timestep: torch.Tensor, text: torch.Tensor, out: torch.Tensor = None,
+                stream=None) -> torch.Tensor:
+        if out is None:
+            b, _, f, hz, wz = latent.shape
+            out = torch.empty((b, self.config.out_channels, f, hz, wz), dtype=latent.dtype, device=latent.device)
+        lt, tt, xt, ot = (as_wan_tensor(latent), as_wan_tensor(timestep), as_wan_tensor(text), as_wan_tensor(out))
+        _check(_forward(self._h, C.byref(lt), C.byref(tt), C.byref(xt), C.byref(ot), _stream(stream)))
+        return out
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------------------------
+# per-stage ops (tensors are torch device tensors; bf16 tensors use torch.bfloat16)
+# ------------------------------------------------------------------------------------------------
+
+
+def op_patchify(latent: torch.Tensor, kp: int, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    b, c, f, hz, wz = latent.shape
+    rows = b * f * (hz // 2) * (wz // 2)
+    if out is None:
+        out = torch.empty((rows, kp), dtype=torch.bfloat16, device=latent.device)
+    _check(_op_patchify(latent.data_ptr(), _dtype_code(latent), b, c, f, hz, wz, kp, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def op_unpatchify(z: torch.Tensor, b: int, c: int, f: int, hz: int, wz: int, dtype=torch.float32, stream=None):
+    out = torch.empty((b, c, f, hz, wz), dtype=dtype, device=z.device)
+    _check(_op_unpatchify(z.data_ptr(), z.shape[1], b, c, f, hz, wz, out.data_ptr(), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def op_gemm(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor, epilogue: int, out: torch.Tensor,
+            gate_tab: torch.Tensor = None, gate_src: torch.Tensor = None, gate_ld: int = 0, rows_per_gate: int = 1,
+            stream=None):
+    m, k = x.shape
+    n = w.shape[0]
+    _check(_op_gemm(x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), bias.data_ptr(), m, n, k, epilogue,
+                    out.data_ptr(), out.stride(0), _ptr(gate_tab), _ptr(gate_src), gate_ld, rows_per_gate,
+                    _stream(stream)))
+    return out
+
+
+def op_layernorm(x: torch.Tensor, eps: float, mode: int, out: torch.Tensor, tab_shift=None, tab_scale=None, src=None,
+                 src_ld=0, src_shift_off=0, src_scale_off=0, rows_per_src=1, gamma=None, beta=None, stream=None):
+    rows, d = x.shape
+    _check(_op_layernorm(x.data_ptr(), rows, d, eps, mode, _ptr(tab_shift), _ptr(tab_scale), _ptr(src), src_ld,
+                         src_shift_off, src_scale_off, rows_per_src, _ptr(gamma), _ptr(beta), out.data_ptr(),
+                         _stream(stream)))
+    return out
+
+
+def op_rope_table(fp: int, hp: int, wp: int, dims=(44, 42, 42), theta: float = 1e4, device="cuda", stream=None):
+    n = int(_op_rope_table_floats(fp, hp, wp, *dims))
+    tab = torch.empty(n, dtype=torch.float32, device=device)
+    _check(_op_rope_table(tab.data_ptr(), fp, hp, wp, *dims, theta, _stream(stream)))
+    return tab
+
+
+def op_qk_norm_rope(buf: torch.Tensor, d: int, eps: float, off_a: int, gamma_a: torch.Tensor, off_b: int = 0,
+                    gamma_b: torch.Tensor = None, table: torch.Tensor = None, L: int = 1, grid=(1, 1, 1),
+                    dims=(44, 42, 42), stream=None):
+    rows = buf.shape[0]
+    _check(_op_qk_norm_rope(buf.data_ptr(), buf.stride(0), rows, d, eps, off_a, gamma_a.data_ptr(), off_b,
+                            _ptr(gamma_b), _ptr(table), L, *grid, *dims, _stream(stream)))
+    return buf
+
+
+def op_transpose_v(src: torch.Tensor, col_off: int, b: int, L: int, nh: int, ldv: int, stream=None):
+    vt = torch.empty((b, nh, 128, ldv), dtype=torch.bfloat16, device=src.device)
+    _check(_op_transpose_v(src.data_ptr(), src.stride(0), col_off, b, L, nh, vt.data_ptr(), ldv, _stream(stream)))
+    return vt
+
+
+def op_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Tensor, b: int, lq: int, lkv: int,
+                 nh: int, stream=None):
+    """q, k, out: 2-D views [b*L, >= 128*nh] (row stride from the tensor); vt [b, nh, 128, ldv]."""
+    _check(_op_attention(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(), vt.shape[3],
+                         out.data_ptr(), out.stride(0), b, lq, lkv, nh, _stream(stream)))
+    return out
+
+
+def op_time_embed(t: torch.Tensor, freq_dim: int, d: int, w1, b1, w2, b2, wp, bp, stream=None):
+    rows = t.numel()
+    temb = torch.empty((rows, d), dtype=torch.float32, device=t.device)
+    tproj = torch.empty((rows, 6 * d), dtype=torch.float32, device=t.device)
+    work = torch.empty(rows * (freq_dim + d), dtype=torch.float32, device=t.device)
+    _check(_op_time_embed(t.data_ptr(), rows, freq_dim, d, w1.data_ptr(), b1.data_ptr(), w2.data_ptr(), b2.data_ptr(),
+                          wp.data_ptr(), bp.data_ptr(), temb.data_ptr(), tproj.data_ptr(), work.data_ptr(),
+                          _stream(stream)))
+    return temb, tproj

@@ -1,0 +1,56 @@
+// Shared device helpers for the gfx950 kernels: bf16 bit conversions, vector types, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw bf16 bits in memory
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define WAN_DEV __device__ __forceinline__
+
+WAN_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (inputs here are finite).
+WAN_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// two fp32 -> packed bf16x2 (low half = a)
+WAN_DEV uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+WAN_DEV float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+WAN_DEV float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+WAN_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Wave-wide (64 lanes) reductions.
+WAN_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+WAN_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// GELU, tanh form.  0.5 u (1 + tanh z) equals u * sigmoid(2 z), z = sqrt(2/pi) (u + 0.044715 u^3).
+WAN_DEV float gelu_tanh_f(float u) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  float z = k0 * (u + 0.044715f * u * u * u);
+  return u / (1.0f + __expf(-2.0f * z));
+}
+
+WAN_DEV float silu_f(float u) { return u / (1.0f + __expf(-u)); }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

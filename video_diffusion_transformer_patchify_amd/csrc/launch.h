@@ -1,0 +1,38 @@
+// Internal launch functions of the gfx950 kernels (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;
+
+enum { EPI_BF16 = 0, EPI_GELU_BF16 = 1, EPI_F32 = 2, EPI_RES_F32 = 3, EPI_GATE_F32 = 4 };
+
+hipError_t launch_patchify(const void* x, int dtype, int64_t B, int64_t C, int64_t F, int64_t Hz, int64_t Wz,
+                           int64_t kp, bf16_t* p, hipStream_t s);
+hipError_t launch_unpatchify(const float* z, int64_t ldz, int64_t B, int64_t C, int64_t F, int64_t Hz, int64_t Wz,
+                             void* out, int dtype, hipStream_t s);
+hipError_t launch_pack_bf16(const void* src, int dtype, int64_t rows, int64_t cols, int64_t lds, bf16_t* dst,
+                            int64_t ldd, hipStream_t s);
+hipError_t launch_pack_f32(const void* src, int dtype, int64_t n, float* dst, hipStream_t s);
+
+hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64_t ldw, const float* bias, int64_t M,
+                            int64_t N, int64_t K, int epi, void* out, int64_t ldo, const float* gate_tab,
+                            const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, hipStream_t s);
+hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, int64_t M,
+                           int64_t N, int64_t K, float* C, int64_t ldc, int silu_in, int silu_out, hipStream_t s);
+
+hipError_t launch_layernorm(const float* x, int64_t rows, int64_t D, float eps, int mode, const float* tab_shift,
+                            const float* tab_scale, const float* src, int64_t src_ld, int64_t src_shift_off,
+                            int64_t src_scale_off, int64_t rows_per_src, const float* gamma, const float* beta,
+                            bf16_t* y, hipStream_t s);
+hipError_t launch_rms_rope(bf16_t* buf, int64_t ld, int64_t rows, int64_t D, float eps, int64_t off_a,
+                           const float* gamma_a, int64_t off_b, const float* gamma_b, const float* rope, int64_t L,
+                           int Fp, int Hp, int Wp, int dt, int dh, int dw, hipStream_t s);
+hipError_t launch_transpose_v(const bf16_t* src, int64_t ld, int64_t col_off, int64_t B, int64_t L, int nh, bf16_t* vt,
+                              int64_t ldv, hipStream_t s);
+int64_t rope_table_floats(int Fp, int Hp, int Wp, int dt, int dh, int dw);
+hipError_t launch_rope_table(float* tab, int Fp, int Hp, int Wp, int dt, int dh, int dw, double theta, hipStream_t s);
+hipError_t launch_sinusoid(const float* t, int64_t rows, int freq_dim, float* out, hipStream_t s);
+
+hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
+                            bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, hipStream_t s);

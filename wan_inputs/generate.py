@@ -1,6 +1,6 @@
 """Seeded synthetic inputs and weights.
 
-Every tensor gets its own counter-free stream: numpy PCG64 seeded by
+Every tensor gets its own random stream: numpy PCG64 seeded by
 SeedSequence(root_seed, spawn_key=(cfg_id, crc32(name))).  Values are drawn in float32 and then,
 for bf16 tensors, rounded to the nearest bf16 (ties to even) so that the oracle (which upcasts to
 float64) and the GPU path (which consumes the raw bits) see identical numbers.
@@ -35,9 +35,9 @@ def _rng(cfg_id: int, name: str, seed: int = ROOT_SEED) -> np.random.Generator:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16, ties to even; returns uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite inputs: u + 0x8000 stays below 2^32, so uint32 arithmetic cannot wrap
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     return r
 
 
