@@ -116,7 +116,7 @@ def cpu_baseline(cfg, budget_s: float):
     q = O.rms_norm(O.linear(y, w.f64(p + "attn1.to_q.weight"), w.f64(p + "attn1.to_q.bias")), one.eps)
     k = O.rms_norm(O.linear(y, w.f64(p + "attn1.to_k.weight"), w.f64(p + "attn1.to_k.bias")), one.eps)
     v = O.linear(y, w.f64(p + "attn1.to_v.weight"), w.f64(p + "attn1.to_v.bias"))
-    nq = 256
+    nq = 2048
     qh = O.apply_rope(q[0].reshape(L, nh, 128), ang)[:nq]
     kh = O.apply_rope(k[0].reshape(L, nh, 128), ang)
     vh = v[0].reshape(L, nh, 128)

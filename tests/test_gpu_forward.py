@@ -26,7 +26,9 @@ def run_gpu(G, cfg, weights, latent, t, text, **kw):
 
     from video_diffusion_transformer_patchify_amd.harness import upload_weights
 
-    wd = upload_weights(weights, drop=False)
+    n_layers = kw.get("num_layers", cfg.num_layers)
+    names = [n for n in weights.names() if not n.startswith("blocks.") or int(n.split(".")[1]) < n_layers]
+    wd = upload_weights(weights, names=names, drop=False)
     model = G.B.WanDiT(G.B.make_config(cfg, **kw), wd)
     del wd
     out = model.forward(G.to_device(latent), G.to_device(t), G.to_device(text))

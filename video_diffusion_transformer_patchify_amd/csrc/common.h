@@ -14,16 +14,16 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 WAN_DEV float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even (inputs here are finite).
-WAN_DEV bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16, round to nearest, ties to even (hardware conversion).
+WAN_DEV bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
-// two fp32 -> packed bf16x2 (low half = a)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16x2 (low half = a), round to nearest even: one v_cvt_pk_bf16_f32 on gfx950.
 WAN_DEV uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 WAN_DEV float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }

@@ -457,7 +457,7 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
     HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, s),
             "qk norm rope");
     HIP_TRY(launch_transpose_v(h->qkv, 3 * D, 2 * D, B, L, (int)nh, h->vt, ldv, s), "v transpose");
-    HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, s), "self attention");
+    HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s), "self attention");
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_GATE_F32, h->x, D, b.table + 2 * D, h->tproj + 2 * D,
                              6 * D, rows_per_mod, s), "attn1 out");
     // cross-attention
@@ -469,7 +469,7 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
             "kv2");
     HIP_TRY(launch_rms_rope(h->kv2, 2 * D, B * Lt, D, eps, 0, b.gk2, 0, nullptr, nullptr, Lt, 1, 1, 1, dt, dh, dw, s), "k2 norm");
     HIP_TRY(launch_transpose_v(h->kv2, 2 * D, D, B, Lt, (int)nh, h->vt2, ldv2, s), "v2 transpose");
-    HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, s), "cross attention");
+    HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, false, s), "cross attention");
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_RES_F32, h->x, D, nullptr, nullptr, 0, 1, s), "attn2 out");
     // feed-forward
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 3 * D, b.table + 4 * D, h->tproj, 6 * D, 3 * D, 4 * D,
@@ -611,7 +611,7 @@ extern "C" wan_status wan_op_attention(const void* q, int64_t ldq, const void* k
           WAN_ERR_SHAPE, "attention: bad row strides");
   REQUIRE((q && k && vt && o) || B * Lq == 0, WAN_ERR_INVALID_ARG, "attention: NULL pointer");
   HIP_TRY(launch_attention((const bf16_t*)q, ldq, (const bf16_t*)k, ldk, (const bf16_t*)vt, ldv, (bf16_t*)o, ldo, B, Lq, Lkv, nh,
-                           (hipStream_t)stream), "attention");
+                           Lq == Lkv, (hipStream_t)stream), "attention");
   return WAN_OK;
 }
 
