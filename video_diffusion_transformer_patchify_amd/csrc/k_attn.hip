@@ -9,34 +9,41 @@
 //   * A workgroup owns 256 queries of one (batch, head): 4 waves x 64 queries, each wave as two
 //     32-query blocks that share every K and V fragment it reads from LDS (half the LDS traffic per
 //     MFMA of one block per wave).  Q stays in registers.
-//   * Keys are consumed in tiles of 64.  K [key][d] and the pre-transposed V (Vt[b][h][d][key], so a
-//     tile is [d][key]) are copied global -> LDS with gfx950's direct loads (global_load_lds_dwordx4:
-//     lane l of an instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), double buffered,
-//     with no register staging.  The 16-byte chunks of each LDS row are XOR-swizzled so the fragment
-//     reads are free of bank conflicts; the swizzle is applied by choosing which global chunk each
-//     lane fetches.
+//   * K [key][d] and the pre-transposed V (Vt[b][h][d][key], so a tile is [d][key]) are copied
+//     global -> LDS in tiles of 64 keys with gfx950's direct loads (global_load_lds_dwordx4: lane l of
+//     an instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), no register staging, three
+//     buffers: while tile t is consumed, tile t+1 is resident and tile t+2 is in flight.  The 16-byte
+//     chunks of each LDS row are XOR-swizzled so the fragment reads are free of bank conflicts; the
+//     swizzle is applied by choosing which global chunk each lane fetches.
 //   * Scores are formed transposed, S^T = K Q^T: the accumulator's column is the lane's query, so the
 //     probabilities P^T come out of the accumulator already in the B-operand layout of the PV MFMA
 //     (O^T += V^T P^T) once the 32 key rows of a K fragment are taken in the order pi(i), which swaps
 //     bits 2 and 3 of i.  With that order, lane half g holds keys 8g..8g+7 (+16) of each 16-key step.
+//   * Keys are processed in 32-key sub-tiles j, software pipelined: the MFMAs of S(j+1) are issued
+//     together with the exp / row-sum / bf16 packing of S(j), and the PV MFMAs of sub-tile j together
+//     with the row max of S(j+1), so matrix and vector work of one wave overlap.
 //   * Softmax in base 2 with the 1/sqrt(128) scale folded into one FMA per score.  The running max is
-//     only raised when a tile's max exceeds it by more than 8 (log2 units): until then the stale max is
-//     kept (probabilities up to 2^8, exact after the final division because numerator and denominator
-//     share it) and the O rescale is skipped.
-//   * Row max is shared between the two lane halves with one cross-lane exchange per tile; row sums
-//     stay per lane half and are combined once at the end.
-//   * Only the last key tile can be partial; it runs a separately compiled copy of the tile body that
-//     masks keys past the end, so full tiles carry no masking code.
+//     only raised when a sub-tile's max exceeds it by more than 8 (log2 units): until then the stale
+//     max is kept (probabilities up to 2^8, exact after the final division because numerator and
+//     denominator share it) and the O rescale is skipped.
+//   * Row max is shared between the two lane halves with one cross-lane exchange per sub-tile; row
+//     sums stay per lane half and are combined once at the end.
+//   * Only the last sub-tile can be partial; its scores are masked in a peeled copy of the loop body.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
-constexpr int KT = 64;              // keys per tile
+constexpr int KT = 64;              // keys per LDS tile
+constexpr int KS = 32;              // keys per sub-tile
+constexpr int NBUF = 3;             // LDS tile buffers
 constexpr int QWAVE = 64;           // queries per wave (two 32-query blocks)
 constexpr int QB = 4 * QWAVE;       // queries per workgroup
-constexpr int K_TILE_BYTES = KT * 256;    // 64 rows of 128 bf16
+constexpr int K_TILE_BYTES = KT * 256;     // 64 rows of 128 bf16
 constexpr int V_TILE_BYTES = 128 * KT * 2; // 128 rows of 64 bf16
+constexpr int TILE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
 constexpr float RESCALE_LOG2 = 8.0f;
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -69,94 +76,109 @@ struct AttnState {
   float m_run[2], l_run[2];
 };
 
-// One 64-key tile for both 32-query blocks of this wave.
-template <bool MASK>
-__device__ __forceinline__ void attn_tile(AttnState& st, const u32x4 (&qf)[2][8], const char* lk, const char* lv,
-                                          int l32, int g, float c, float grow_thr, int key_lim) {
-  // ---- S^T = K Q^T; each K fragment read once, used by both query blocks
-  f32x16 sacc[2][2];
+// S^T for sub-tile `sub` (0 or 1) of an LDS tile, both query blocks; each K fragment read once.
+__device__ __forceinline__ void scores(f32x16 (&s)[2], const u32x4 (&qf)[2][8], const char* lk, int sub, int l32,
+                                       int g) {
+  const int row = KS * sub + key_perm(l32);
+  const char* kr = lk + row * 256;
+  const int sw = k_swz(row);
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
 #pragma unroll
-  for (int kt2 = 0; kt2 < 2; ++kt2) {
-    sacc[0][kt2] = (f32x16){};
-    sacc[1][kt2] = (f32x16){};
-    const int row = 32 * kt2 + key_perm(l32);
-    const char* kr = lk + row * 256;
-    const int sw = k_swz(row);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 kf = *(const u32x4*)(kr + (((2 * s + g) ^ sw) << 4));
-      sacc[0][kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[0][s]), sacc[0][kt2], 0, 0, 0);
-      sacc[1][kt2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[1][s]), sacc[1][kt2], 0, 0, 0);
-    }
+  for (int st = 0; st < 8; ++st) {
+    u32x4 kf = *(const u32x4*)(kr + (((2 * st + g) ^ sw) << 4));
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[0][st]), s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[1][st]), s[1], 0, 0, 0);
   }
-  // element r of sub-tile kt2 holds key 32 kt2 + 16 (r/8) + 8 g + r%8 of the tile
-  if constexpr (MASK) {
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = 32 * kt2 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (kk >= key_lim) sacc[qb][kt2][r] = -INFINITY;
-        }
-  }
+}
 
-  // ---- online softmax (base 2), per query block
-  u32x4 pf[2][4];
+// Scores of keys >= key_lim (sub-tile relative) become -inf.  Element r holds key 16 (r/8) + 8 g + r%8.
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int g, int key_lim) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 16 * (r >> 3) + 8 * g + (r & 7);
+      if (kk >= key_lim) s[qb][r] = -INFINITY;
+    }
+}
+
+// Row max of a sub-tile's scores for both query blocks (both lane halves agree).
+__device__ __forceinline__ void row_max(f32x16 (&s)[2], float (&mx)[2]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[qb][r];
+      asm volatile("" : "+v"(x));   // one copy out of the accumulator registers, reused by probs()
+      s[qb][r] = x;
+    }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float mx = sacc[qb][0][0];
+    float m = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
+    for (int r = 2; r < 16; ++r) m = fmaxf(m, s[qb][r]);
+    // lanes 0-31 and 32-63 hold the two key halves of the same queries: swap halves and combine
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    mx[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  }
+}
+
+// Raise the running max where a sub-tile's max passed it by more than the margin; rescale O and l.
+__device__ __forceinline__ void maybe_rescale(AttnState& st, const float (&mx)[2], float c, float grow_thr) {
 #pragma unroll
-      for (int r = (kt2 == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, sacc[qb][kt2][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool grow = mx > st.m_run[qb] + grow_thr;
+  for (int qb = 0; qb < 2; ++qb) {
+    const bool grow = mx[qb] > st.m_run[qb] + grow_thr;
     if (__any(grow)) {
-      const float m_new = grow ? mx : st.m_run[qb];
+      const float m_new = grow ? mx[qb] : st.m_run[qb];
       const float alpha = __builtin_amdgcn_exp2f((st.m_run[qb] - m_new) * c);
       st.m_run[qb] = m_new;
       st.l_run[qb] *= alpha;
-      // one 16-register accumulator at a time: the accumulators live in AGPRs and each multiply needs
-      // VGPR temporaries
+      // one 16-register accumulator at a time: they live in AGPRs, each multiply needs VGPR temporaries
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         st.o[qb][dt] *= alpha;
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  }
+}
+
+// P = exp2(s c - m c) as bf16 B-operand fragments (two 16-key steps per query block); l += row sums.
+__device__ __forceinline__ void probs(AttnState& st, const f32x16 (&s)[2], u32x4 (&pf)[2][2], float c) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
     const float mc = -st.m_run[qb] * c;
     float ls = 0.f;
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
+    for (int hh = 0; hh < 2; ++hh) {
+      float p[8];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kt2][8 * hh + e], c, mc));
-          ls += p[e];
-        }
-        u32x4 w;
-        w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]);
-        w.z = pack_bf16x2(p[4], p[5]); w.w = pack_bf16x2(p[6], p[7]);
-        pf[qb][2 * kt2 + hh] = w;
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], c, mc));
+        ls += p[e];
       }
+      u32x4 w;
+      w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]);
+      w.z = pack_bf16x2(p[4], p[5]); w.w = pack_bf16x2(p[6], p[7]);
+      pf[qb][hh] = w;
+    }
     st.l_run[qb] += ls;
   }
+}
 
-  // ---- O^T += V^T P^T: A = Vt rows d = 32 dt + l32, keys 16 j + 8 g .. +7; each V fragment read once
+// O^T += V^T P^T for sub-tile `sub` of an LDS tile: A = Vt rows d = 32 dt + l32, keys 32 sub + 16 jj + 8 g.
+__device__ __forceinline__ void pv(AttnState& st, const u32x4 (&pf)[2][2], const char* lv, int sub, int l32, int g) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const int row = 32 * dt + l32;
     const char* vr = lv + row * 128;
     const int sw = v_swz(row);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 vf = *(const u32x4*)(vr + (((2 * j + g) ^ sw) << 4));
-      st.o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[0][j]), st.o[0][dt], 0, 0, 0);
-      st.o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[1][j]), st.o[1][dt], 0, 0, 0);
+    for (int jj = 0; jj < 2; ++jj) {
+      u32x4 vf = *(const u32x4*)(vr + (((2 * (2 * sub + jj) + g) ^ sw) << 4));
+      st.o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[0][jj]), st.o[0][dt], 0, 0, 0);
+      st.o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[1][jj]), st.o[1][dt], 0, 0, 0);
     }
   }
 }
@@ -165,7 +187,7 @@ __device__ __forceinline__ void attn_tile(AttnState& st, const u32x4 (&qf)[2][8]
 // a trace); the code path is the same.
 template <bool SELF>
 __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2][K_TILE_BYTES + V_TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -185,7 +207,12 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     const int64_t qrow = qi[qb] < a.Lq ? qi[qb] : a.Lq - 1;
     const bf16_t* qp = a.q + ((int64_t)b * a.Lq + qrow) * a.ldq + h * 128 + g * 8;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[qb][s] = *(const u32x4*)(qp + 16 * s);
+    for (int s = 0; s < 8; ++s) {
+      u32x4 v = *(const u32x4*)(qp + 16 * s);
+      // MFMA source operands may come from AGPRs: Q lives there for the whole kernel, which leaves
+      // the VGPRs to the score copies the softmax works on
+      asm volatile("; q fragment %0" : "=a"(qf[qb][s]) : "0"(v));
+    }
   }
 
   // ---- direct global -> LDS copies.  Each wave issues 4 K and 4 V instructions per tile.
@@ -194,31 +221,43 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   const bf16_t* kbase = a.k + (int64_t)b * a.Lkv * a.ldk + h * 128;
   const bf16_t* vbase = a.vt + ((int64_t)b * a.nh + h) * 128 * a.ldv;
   const int n_tiles = (int)((a.Lkv + KT - 1) / KT);
-  int k_row[4], k_col[4], v_row[4], v_col[4];
+  const int n_sub = (int)((a.Lkv + KS - 1) / KS);
+  // per-lane byte offsets inside a tile (K rows of the tile, Vt rows), fixed for the whole loop
+  uint32_t k_off[4], v_off[4];
+  int k_row[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int I = 4 * wave + i;
     k_row[i] = 4 * I + (lane >> 4);
-    k_col[i] = ((lane & 15) ^ k_swz(k_row[i])) * 8;
-    v_row[i] = 8 * I + (lane >> 3);
-    v_col[i] = ((lane & 7) ^ v_swz(v_row[i])) * 8;
+    const int k_col = ((lane & 15) ^ k_swz(k_row[i])) * 8;
+    k_off[i] = (uint32_t)(((int64_t)k_row[i] * a.ldk + k_col) * 2);
+    const int v_row = 8 * I + (lane >> 3);
+    const int v_col = ((lane & 7) ^ v_swz(v_row)) * 8;
+    v_off[i] = (uint32_t)(((int64_t)v_row * a.ldv + v_col) * 2);
   }
-  auto issue = [&](int t, int buf) {
+  const bool tail_rows = (a.Lkv % KT) != 0;
+  auto issue = [&](int t) {
     const int64_t key0 = (int64_t)t * KT;
-    char* lk = lds[buf];
-    char* lv = lds[buf] + K_TILE_BYTES;
+    char* lk = lds[t % NBUF];
+    char* lv = lk + K_TILE_BYTES;
+    const char* kt = (const char*)(kbase + key0 * a.ldk);
+    const char* vtb = (const char*)(vbase + key0);
+    if (tail_rows && t == n_tiles - 1) {
+      // last, partial tile: rows past the end re-read the last valid row (their scores are masked)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t key = key0 + k_row[i];
-      if (key > a.Lkv - 1) key = a.Lkv - 1;      // rows past the end are masked in the last tile
-      __builtin_amdgcn_global_load_lds((const void*)(kbase + key * a.ldk + k_col[i]),
-                                       (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = key0 + k_row[i] < a.Lkv ? k_row[i] : a.Lkv - 1 - key0;
+        const uint32_t off = (uint32_t)(k_off[i] + (key - k_row[i]) * a.ldk * 2);
+        __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(kt + k_off[i]), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds((const void*)(vbase + (int64_t)v_row[i] * a.ldv + key0 + v_col[i]),
-                                       (lds_void*)(lv + (4 * wave + i) * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(vtb + v_off[i]), (lds_void*)(lv + (4 * wave + i) * 1024), 16, 0, 0);
   };
 
   AttnState st;
@@ -231,21 +270,52 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   }
   const float c = a.scale_log2;
   const float grow_thr = RESCALE_LOG2 / c;   // raw-score margin before the max is raised
-  const int n_full = (int)(a.Lkv / KT);
+  const int last_lim = (int)(a.Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
 
-  issue(0, 0);
+  // ---- prologue: tiles 0 and 1 resident, scores and max of sub-tile 0
+  issue(0);
+  if (n_tiles > 1) issue(1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < n_full; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) issue(t + 1, buf ^ 1);
-    attn_tile<false>(st, qf, lds[buf], lds[buf] + K_TILE_BYTES, l32, g, c, grow_thr, KT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  f32x16 s_cur[2], s_next[2];
+  float mx[2];
+  scores(s_cur, qf, lds[0], 0, l32, g);
+  if (n_sub == 1 && last_lim < KS) mask_scores(s_cur, g, last_lim);
+  row_max(s_cur, mx);
+  maybe_rescale(st, mx, c, grow_thr);
+
+  // One pipelined step: S(j+1) with P(j); PV(j) with max(S(j+1)).  LAST: S(j+1) is the final sub-tile.
+  auto step = [&](int j, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int t = j >> 1, half = j & 1;
+    if (!half && t + 2 < n_tiles) issue(t + 2);
+    u32x4 pf[2][2];
+    scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
+    probs(st, s_cur, pf, c);
+    if constexpr (LAST) {
+      if (last_lim < KS) mask_scores(s_next, g, last_lim);
+    }
+    pv(st, pf, lds[t % NBUF] + K_TILE_BYTES, half, l32, g);
+    row_max(s_next, mx);
+    maybe_rescale(st, mx, c, grow_thr);
+    if (half) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) s_cur[qb] = s_next[qb];
+  };
+  int j = 0;
+  for (; j + 2 < n_sub; ++j) step(j, std::false_type{});
+  if (j + 1 < n_sub) {
+    step(j, std::true_type{});
+    ++j;
   }
-  if (n_full < n_tiles) {   // partial last tile, already in LDS
-    const int buf = n_full & 1;
-    attn_tile<true>(st, qf, lds[buf], lds[buf] + K_TILE_BYTES, l32, g, c, grow_thr, (int)(a.Lkv - (int64_t)n_full * KT));
+  // ---- last sub-tile j = n_sub - 1
+  {
+    u32x4 pf[2][2];
+    probs(st, s_cur, pf, c);
+    pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
   }
 
   // ---- normalise and store: o[qb][dt] element r holds d = 32 dt + 8 (r/4) + 4 g + r%4 of query qi[qb]
