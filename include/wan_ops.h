@@ -42,15 +42,21 @@ wan_status wan_op_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, c
                        int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
                        const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, void* stream);
 
-/* LayerNorm over D (population variance, eps) of fp32 rows x [rows, D] -> bf16 y [rows, D]:
- *   mode 0 (norm1 / norm3 / norm_out + modulation; WanPipeline notes, block and output head):
- *     y = LN(x) * (1 + tab_scale[d] + src[r*src_ld + src_scale_off + d])
- *               + tab_shift[d] + src[r*src_ld + src_shift_off + d],   r = row / rows_per_src
+/* Residual add + LayerNorm over D (population variance, eps) of fp32 rows x [rows, D] -> bf16 y [rows, D]
+ * (WanPipeline notes, WanTransformerBlock: hidden_states + attn_output * gate_msa, + attn_output,
+ * + ff_output * c_gate_msa, each followed by the next norm).  With r = res [rows, D] bf16 and
+ * s = row / rows_per_src:
+ *   res_mode 1: x += r;   res_mode 2: x += r * (res_tab[d] + res_src[s*res_ld + d]);   x is updated in place.
+ * Then:
+ *   mode 0 (norm1 / norm3 / norm_out + modulation; block and output head):
+ *     y = LN(x) * (1 + tab_scale[d] + src[s*src_ld + src_scale_off + d])
+ *               + tab_shift[d] + src[s*src_ld + src_shift_off + d]
  *   mode 1 (norm2 with affine, cross_attn_norm): y = LN(x) * gamma[d] + beta[d]
  * D multiple of 256, at most 6144. */
-wan_status wan_op_layernorm(const float* x, int64_t rows, int64_t D, float eps, int32_t mode, const float* tab_shift,
+wan_status wan_op_layernorm(float* x, int64_t rows, int64_t D, float eps, int32_t mode, const float* tab_shift,
                             const float* tab_scale, const float* src, int64_t src_ld, int64_t src_shift_off,
                             int64_t src_scale_off, int64_t rows_per_src, const float* gamma, const float* beta,
+                            int32_t res_mode, const void* res, const float* res_tab, const float* res_src, int64_t res_ld,
                             void* y, void* stream);
 
 /* Size in floats of the RoPE angle table for a (Fp, Hp, Wp) token grid and head-dim split

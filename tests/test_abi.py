@@ -68,6 +68,9 @@ def test_validation_errors_without_gpu():
     assert B._op_gemm(1, 64, 1, 64, 1, 10, 64, 64, 4, 1, 64, None, None, 0, 1, None) == 1      # gate missing
     assert B._op_patchify(1, 0, 1, 16, 5, 15, 16, 64, 1, None) == 2                             # odd height
     assert B._op_attention(1, 1536, 1, 1536, 1, 100, 1, 1536, 1, 320, 320, 12, None) == 2       # ldv < Lkv
-    assert B._op_layernorm(1, 4, 1000, 1e-6, 0, 1, 1, 1, 0, 0, 0, 1, None, None, 1, None) == 2  # D % 256
+    assert B._op_layernorm(1, 4, 1000, 1e-6, 0, 1, 1, 1, 0, 0, 0, 1, None, None, 0, None, None, None, 0, 1,
+                           None) == 2                                                           # D % 256
+    assert B._op_layernorm(1, 4, 1536, 1e-6, 0, 1, 1, 1, 0, 0, 0, 1, None, None, 2, 1, None, None, 0, 1,
+                           None) == 1                                                           # gate missing
     assert B._op_qk_norm_rope(1, 4608, 4, 1536, 1e-6, 0, 1, 1536, 1, 1, 10, 2, 2, 2, 44, 42, 42, None) == 2
     assert B._op_rope_table(1, 5, 8, 8, 44, 42, 40, 1e4, None) == 2                              # dims sum != 128

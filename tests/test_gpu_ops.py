@@ -354,3 +354,34 @@ def test_time_embed(G, rows, D, per_token):
     r_temb, r_tproj = O.time_embed(t_h, w)
     assert G.rel_l2(G.to_f64(temb), r_temb) < 1e-4
     assert G.rel_l2(G.to_f64(tproj), r_tproj.reshape(rows, 6 * D)) < 1e-4
+
+
+@pytest.mark.parametrize("rows,D,res_mode,per_token", [(300, 1536, 1, False), (1000, 3072, 2, False),
+                                                       (257, 5120, 2, True), (65520, 1536, 2, False)])
+def test_layernorm_with_residual(G, rows, D, res_mode, per_token):
+    """x += r (res_mode 1) or x += r * (tab + src[row]) (res_mode 2), then LN + modulation."""
+    import torch
+
+    G.note(f"layernorm residual rows={rows} D={D} res_mode={res_mode} per_token={per_token}")
+    xt = G.draw_normal(4, f"lrx{rows}{D}", (rows, D), "f32", 1.5)
+    x = G.to_device(xt).clone()
+    r, rh = G.bf16_dev((rows, D), f"lrr{rows}{D}", 0.7)
+    L = 1 if per_token else 100
+    nsrc = (rows + L - 1) // L
+    tab_t = G.draw_normal(4, "lrtab", (6, D), "f32", 1.0 / math.sqrt(D))
+    src_t = G.draw_normal(4, f"lrsrc{nsrc}{D}", (nsrc, 6 * D), "f32", 0.3)
+    tab, src = G.to_device(tab_t), G.to_device(src_t)
+    y = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+    G.B.op_layernorm(x, 1e-6, 0, y, tab_shift=tab[0], tab_scale=tab[1], src=src, src_ld=6 * D, src_shift_off=0,
+                     src_scale_off=D, rows_per_src=L, res_mode=res_mode, res=r, res_tab=tab[2],
+                     res_src=src[:, 2 * D:], res_ld=6 * D)
+    G.sync()
+    s = src_t.f64()[np.arange(rows) // L]
+    gate = tab_t.f64()[2] + s[:, 2 * D:3 * D]
+    x_ref = xt.f64() + (rh * gate if res_mode == 2 else rh)
+    x_got = G.to_f64(x)
+    # fp32 update: one rounding of the sum
+    assert np.abs(x_got - x_ref).max() <= 2.0 ** -22 * np.abs(x_ref).max()
+    ref = O.layer_norm(x_ref, 1e-6) * (1.0 + tab_t.f64()[1] + s[:, D:2 * D]) + tab_t.f64()[0] + s[:, :D]
+    got = G.to_f64(y)
+    assert G.rel_l2(got, ref) < 3e-3

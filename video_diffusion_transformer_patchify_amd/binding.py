@@ -68,7 +68,7 @@ _op_unpatchify = _sig("wan_op_unpatchify", [_vp, _i64, _i64, _i64, _i64, _i64, _
 _op_gemm = _sig("wan_op_gemm", [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
                                 _vp])
 _op_layernorm = _sig("wan_op_layernorm", [_vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp,
-                                          _vp, _vp, _vp])
+                                          _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp])
 _op_rope_table_floats = _sig("wan_op_rope_table_floats", [_i32] * 6, _i64)
 _op_rope_table = _sig("wan_op_rope_table", [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _f64, _vp])
 _op_qk_norm_rope = _sig("wan_op_qk_norm_rope", [_vp, _i64, _i64, _i64, _f32, _i64, _vp, _i64, _vp, _vp, _i64, _i32,
@@ -220,11 +220,13 @@ def op_gemm(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor, epilogue: int,
 
 
 def op_layernorm(x: torch.Tensor, eps: float, mode: int, out: torch.Tensor, tab_shift=None, tab_scale=None, src=None,
-                 src_ld=0, src_shift_off=0, src_scale_off=0, rows_per_src=1, gamma=None, beta=None, stream=None):
+                 src_ld=0, src_shift_off=0, src_scale_off=0, rows_per_src=1, gamma=None, beta=None, res_mode=0,
+                 res=None, res_tab=None, res_src=None, res_ld=0, stream=None):
+    """x (fp32, updated in place when res_mode > 0) -> out (bf16)."""
     rows, d = x.shape
     _check(_op_layernorm(x.data_ptr(), rows, d, eps, mode, _ptr(tab_shift), _ptr(tab_scale), _ptr(src), src_ld,
-                         src_shift_off, src_scale_off, rows_per_src, _ptr(gamma), _ptr(beta), out.data_ptr(),
-                         _stream(stream)))
+                         src_shift_off, src_scale_off, rows_per_src, _ptr(gamma), _ptr(beta), res_mode, _ptr(res),
+                         _ptr(res_tab), _ptr(res_src), res_ld, out.data_ptr(), _stream(stream)))
     return out
 
 

@@ -5,22 +5,23 @@
 // X is the activation (row-major, K contiguous), W an nn.Linear weight [N, K] (K contiguous), so both
 // operands are read 16 bytes per lane straight into MFMA fragments.  The MFMA "A" operand is a W tile
 // and the "B" operand an X tile, i.e. every 32x32 accumulator holds C^T: each lane then owns four
-// consecutive output columns of one row, which makes the epilogue's stores and the fp32 residual
-// read-modify-write 16-byte vector accesses.
+// consecutive output columns of one row, which makes the epilogue's stores 8- or 16-byte vector accesses.
 //
-// Epilogues (diffusers WanTransformerBlock.forward as printed on the WanPipeline notes page):
-//   EPI_BF16       out_bf16 = acc + bias                                  (QKV, cross Q/KV, text proj)
+// Epilogues (every nn.Linear of WanTransformerBlock.forward as printed on the WanPipeline notes page):
+//   EPI_BF16       out_bf16 = acc + bias
 //   EPI_GELU_BF16  out_bf16 = gelu_tanh(acc + bias)                       (FFN first Linear, text proj)
 //   EPI_F32        out_f32  = acc + bias                                  (patch embed, proj_out)
-//   EPI_RES_F32    out_f32 += acc + bias                                  (ungated cross-attn residual)
-//   EPI_GATE_F32   out_f32 += (acc + bias) * (gate_tab[n] + gate_src[row(m)][n])   (gate_msa, c_gate_msa)
+//   EPI_RES_F32    out_f32 += acc + bias
+//   EPI_GATE_F32   out_f32 += (acc + bias) * (gate_tab[n] + gate_src[row(m)][n])
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDS_LD = BK + 8;  // bf16 per LDS row: 144 B rows keep ds_read_b128 conflict-free
+constexpr int LDS_LD = BK + 8;  // bf16 per LDS row in the small kernel: 144 B rows, conflict-free reads
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemmArgs {
   const bf16_t* x; int64_t ldx;
@@ -36,44 +37,83 @@ struct GemmArgs {
 };
 
 // Dispatch order places consecutive workgroups on different XCDs (round robin over 8).  Renumber so
-// that each XCD receives a contiguous range of logical tiles: tiles that share X rows then share
-// that XCD's L2.
+// that each XCD receives a contiguous range of logical tiles.
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   const int per = nb / 8, rem = nb % 8;
   const int xcd = b % 8, slot = b / 8;
   return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-template <int EPI>
-__device__ __forceinline__ void epilogue4(const GemmArgs& a, int64_t m, int64_t n, f32x4 v) {
-  // v holds columns n..n+3 of row m; caller guarantees m < M and n + 3 < N.
-  f32x4 b = *(const f32x4*)(a.bias + n);
-  v += b;
-  if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16) {
-    if constexpr (EPI == EPI_GELU_BF16) {
-      v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+// Epilogue of a wave's (32 TN) x (32 TM) output block.  acc[i][j] element r holds
+// n = nb + 32 i + 8 (r/4) + 4 g + r%4, m = mb + 32 j + l32.  All bias fragments are loaded up front;
+// for read-modify-write epilogues each row group's operands are fetched before any of it is used, so
+// those loads are in flight together instead of one latency per 4 outputs.
+template <int EPI, int TN, int TM>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const f32x16 (&acc)[TN][TM], int64_t mb, int64_t nb, int l32,
+                                           int g) {
+  f32x4 bias[TN][4];
+  const bool full_n = nb + 32 * TN <= a.N;
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      int64_t n = nb + 32 * i + 8 * rg + 4 * g;
+      if (!full_n && n >= a.N) n = a.N - 4;
+      bias[i][rg] = *(const f32x4*)(a.bias + n);
     }
-    u32x2 o;
-    o.x = pack_bf16x2(v.x, v.y);
-    o.y = pack_bf16x2(v.z, v.w);
-    *(u32x2*)((bf16_t*)a.out + m * a.ldo + n) = o;
-  } else if constexpr (EPI == EPI_F32) {
-    *(f32x4*)((float*)a.out + m * a.ldo + n) = v;
-  } else if constexpr (EPI == EPI_RES_F32) {
-    f32x4* p = (f32x4*)((float*)a.out + m * a.ldo + n);
-    *p = *p + v;
-  } else {  // EPI_GATE_F32
-    const int64_t gr = m / a.rows_per_gate;
-    f32x4 g = *(const f32x4*)(a.gate_tab + n) + *(const f32x4*)(a.gate_src + gr * a.gate_ld + n);
-    f32x4* p = (f32x4*)((float*)a.out + m * a.ldo + n);
-    *p = *p + v * g;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const int64_t m = mb + 32 * j + l32;
+    const bool row_ok = m < a.M;
+    const int64_t mr = row_ok ? m : a.M - 1;
+    f32x4 old[TN][4], gate[TN][4];
+    if constexpr (EPI == EPI_RES_F32 || EPI == EPI_GATE_F32) {
+      const int64_t gr = mr / a.rows_per_gate;
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          int64_t n = nb + 32 * i + 8 * rg + 4 * g;
+          if (!full_n && n >= a.N) n = a.N - 4;
+          old[i][rg] = *(const f32x4*)((const float*)a.out + mr * a.ldo + n);
+          if constexpr (EPI == EPI_GATE_F32)
+            gate[i][rg] = *(const f32x4*)(a.gate_tab + n) + *(const f32x4*)(a.gate_src + gr * a.gate_ld + n);
+        }
+    }
+    if (!row_ok) continue;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int64_t n = nb + 32 * i + 8 * rg + 4 * g;
+        if (!full_n && n >= a.N) continue;
+        f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
+        v += bias[i][rg];
+        if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16) {
+          if constexpr (EPI == EPI_GELU_BF16) {
+            v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+          }
+          u32x2 o;
+          o.x = pack_bf16x2(v.x, v.y);
+          o.y = pack_bf16x2(v.z, v.w);
+          *(u32x2*)((bf16_t*)a.out + m * a.ldo + n) = o;
+        } else if constexpr (EPI == EPI_F32) {
+          *(f32x4*)((float*)a.out + m * a.ldo + n) = v;
+        } else if constexpr (EPI == EPI_RES_F32) {
+          *(f32x4*)((float*)a.out + m * a.ldo + n) = old[i][rg] + v;
+        } else {
+          *(f32x4*)((float*)a.out + m * a.ldo + n) = old[i][rg] + v * gate[i][rg];
+        }
+      }
   }
 }
 
-// BM x BN workgroup tile, 4 waves arranged (BM/WM) x (BN/WN), each wave a WM x WN tile built from
-// 32x32x16 bf16 MFMAs.  K must be a multiple of 64; M and N tails are clamped on load, guarded on store.
+// ---------------------------------------------------------------------------------------------------
+// Small-problem kernel: BM x BN workgroup tile, 4 waves of WM x WN, register-staged copies into padded
+// LDS rows, double buffered.  M and N tails are clamped on load and guarded on store.
+// ---------------------------------------------------------------------------------------------------
 template <int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256, (BM >= 256 ? 1 : 2)) void k_gemm_bf16(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmArgs a) {
   static_assert((BM / WM) * (BN / WN) == 4, "4 waves");
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int XCH = BM * BK / 8 / 256;  // 16-byte chunks per thread for the X tile
@@ -88,7 +128,6 @@ __global__ __launch_bounds__(256, (BM >= 256 ? 1 : 2)) void k_gemm_bf16(GemmArgs
   const int wm0 = (wave / (BN / WN)) * WM, wn0 = (wave % (BN / WN)) * WN;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // global load addressing: chunk c = tid + 256*i covers row c/8, 8 bf16 at column (c%8)*8
   const bf16_t* xp[XCH];
   const bf16_t* wp[WCH];
 #pragma unroll
@@ -150,23 +189,106 @@ __global__ __launch_bounds__(256, (BM >= 256 ? 1 : 2)) void k_gemm_bf16(GemmArgs
     if (kt + 1 < nk) lstore(buf ^ 1);
     __syncthreads();
   }
+  store_tile<EPI, TN, TM>(a, acc, m0 + wm0, n0 + wn0, l32, g);
+}
 
-  // acc[i][j] element r: n = n0 + wn0 + 32i + 8(r/4) + 4g + r%4, m = m0 + wm0 + 32j + l32
+// ---------------------------------------------------------------------------------------------------
+// Large-problem kernel: 256 x 256 x 64 tiles, 4 waves of 128 x 128, operands copied global -> LDS with
+// gfx950's direct loads (global_load_lds_dwordx4: lane l of an instruction fills bytes 16 l .. 16 l + 15
+// of a 1 KB LDS block), double buffered, no register staging.  Each 128-byte LDS row (64 bf16 of K)
+// holds its eight 16-byte chunks XOR-swizzled by swz(row) so fragment reads are free of bank
+// conflicts; the swizzle is applied by choosing which global chunk each lane fetches.  Tiles are
+// visited in groups of GROUP_M tile rows so the tiles that run together on one XCD share A rows and
+// B columns in its L2.
+// ---------------------------------------------------------------------------------------------------
+constexpr int BIG = 256;
+constexpr int GROUP_M = 8;
+constexpr int OPND_BYTES = BIG * BK * 2;        // one operand tile, 32 KB
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;     // X tile then W tile
+
+__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[2][STAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // ---- tile order: XCD-contiguous ranges, grouped by GROUP_M tile rows
+  const int nb = a.tiles_m * a.tiles_n;
+  const int tile = xcd_remap(blockIdx.x, nb);
+  const int width = GROUP_M * a.tiles_n;
+  const int first_m = (tile / width) * GROUP_M;
+  const int gsz = min(a.tiles_m - first_m, GROUP_M);
+  const int tm = first_m + (tile % width) % gsz;
+  const int tn = (tile % width) / gsz;
+  const int64_t m0 = (int64_t)tm * BIG, n0 = (int64_t)tn * BIG;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+
+  // ---- direct-load addressing: instruction I = 8 wave + i covers tile rows 8 I .. 8 I + 7;
+  //      lane -> row 8 I + lane / 8, LDS chunk position lane % 8, global chunk (lane % 8) ^ swz(row).
+  uint32_t xo[8], wo[8];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int64_t m = m0 + wm0 + 32 * j + l32;
-    if (m >= a.M) continue;
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int64_t n = n0 + wn0 + 32 * i + 8 * rg + 4 * g;
-        if (n >= a.N) continue;
-        f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
-        epilogue4<EPI>(a, m, n, v);
-      }
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int r = 8 * (8 * wave + i) + (lane >> 3);
+    const int cchunk = (lane & 7) ^ row_swz(r);
+    int64_t rx = m0 + r, rw = n0 + r;
+    if (rx > a.M - 1) rx = a.M - 1;        // rows past the end repeat the last row (never stored)
+    if (rw > a.N - 1) rw = a.N - 1;
+    xo[i] = (uint32_t)(((rx - m0) * a.ldx + cchunk * 8) * 2);
+    wo[i] = (uint32_t)(((rw - n0) * a.ldw + cchunk * 8) * 2);
   }
+  const char* xt = (const char*)(a.x + m0 * a.ldx);
+  const char* wt = (const char*)(a.w + n0 * a.ldw);
+  auto issue = [&](int kt, int buf) {
+    char* lx = lds[buf];
+    char* lw = lds[buf] + OPND_BYTES;
+    const int kb = kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(xt + kb + xo[i]), (lds_void*)(lx + (8 * wave + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(wt + kb + wo[i]), (lds_void*)(lw + (8 * wave + i) * 1024), 16, 0, 0);
+  };
+
+  // ---- fragment read offsets: rows (multiples of 32) + l32 share the swizzle of l32
+  int foff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) foff[ks] = l32 * 128 + (((2 * ks + g) ^ row_swz(l32)) << 4);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+
+  const int nk = (int)(a.K / BK);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
+    const char* lx = lds[buf] + wm0 * 128;
+    const char* lw = lds[buf] + OPND_BYTES + wn0 * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const u32x4*)(lw + i * 32 * 128 + foff[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *(const u32x4*)(lx + j * 32 * 128 + foff[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  store_tile<EPI, 4, 4>(a, acc, m0 + wm0, n0 + wn0, l32, g);
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -180,6 +302,21 @@ hipError_t launch_tile(int epi, GemmArgs& a, hipStream_t s) {
     case EPI_F32: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_F32>), grid, block, 0, s, a); break;
     case EPI_RES_F32: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_RES_F32>), grid, block, 0, s, a); break;
     case EPI_GATE_F32: hipLaunchKernelGGL((k_gemm_bf16<BM, BN, WM, WN, EPI_GATE_F32>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_big(int epi, GemmArgs& a, hipStream_t s) {
+  a.tiles_m = (int)ceil_div(a.M, BIG);
+  a.tiles_n = (int)ceil_div(a.N, BIG);
+  dim3 grid(a.tiles_m * a.tiles_n), block(256);
+  switch (epi) {
+    case EPI_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_BF16>, grid, block, 0, s, a); break;
+    case EPI_GELU_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_GELU_BF16>, grid, block, 0, s, a); break;
+    case EPI_F32: hipLaunchKernelGGL(k_gemm_big<EPI_F32>, grid, block, 0, s, a); break;
+    case EPI_RES_F32: hipLaunchKernelGGL(k_gemm_big<EPI_RES_F32>, grid, block, 0, s, a); break;
+    case EPI_GATE_F32: hipLaunchKernelGGL(k_gemm_big<EPI_GATE_F32>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -200,7 +337,6 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
   const int tr = tid / 16, tc = tid % 16;
   float acc[4][4] = {};
   for (int64_t k0 = 0; k0 < K; k0 += KB) {
-    // 64 rows x 16 k per operand = 1024 elements, 4 per thread
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int e = tid + 256 * i;
@@ -250,10 +386,11 @@ hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64
   a.M = M; a.N = N; a.K = K; a.out = out; a.ldo = ldo;
   a.gate_tab = gate_tab; a.gate_src = gate_src; a.gate_ld = gate_ld;
   a.rows_per_gate = rows_per_gate > 0 ? rows_per_gate : 1;
-  // Large problems: 256x256 tiles (each wave 128x128, 16 MFMA tiles in flight per LDS fragment set).
-  // Small ones: 128x128 so the grid still covers the chip.
+  // Large problems: 256x256 tiles with direct LDS loads.  Small ones: 128x128 so the grid still covers
+  // the chip.  The direct-load offsets are 32-bit: 256 rows of the larger leading dimension must fit.
   const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
-  if (big_tiles >= 512) return launch_tile<256, 256, 128, 128>(epi, a, s);
+  const bool offsets_fit = 256 * (ldx > ldw ? ldx : ldw) * 2 < (1LL << 31);
+  if (big_tiles >= 512 && offsets_fit) return launch_big(epi, a, s);
   return launch_tile<128, 128, 64, 64>(epi, a, s);
 }
 

@@ -15,15 +15,20 @@
 namespace {
 
 // ---------------------------------------------------------------------------------------------------
-// LayerNorm + modulate / affine.  One wave per row; NV float4 per lane (D = 256 * NV).
+// Residual add + LayerNorm + modulate / affine.  One wave per row; NV float4 per lane (D = 256 * NV).
+// The residual step folds the previous branch into the fp32 stream before normalising it:
+//   res_mode 1: x += r            (cross-attention output, ungated)
+//   res_mode 2: x += r * gate,    gate = res_tab[d] + res_src[row(m)][d]   (gate_msa, c_gate_msa)
+// and writes x back; r is the bf16 output of the branch's last Linear.
 // ---------------------------------------------------------------------------------------------------
 struct LnArgs {
-  const float* x; int64_t rows; int64_t D; float eps;
+  float* x; int64_t rows; int64_t D; float eps;
   int mode;                       // 0: modulate, 1: affine
   const float* tab_shift;         // [D]
   const float* tab_scale;         // [D]
   const float* src; int64_t src_ld; int64_t src_shift_off; int64_t src_scale_off; int64_t rows_per_src;
   const float* gamma; const float* beta;
+  int res_mode; const bf16_t* res; const float* res_tab; const float* res_src; int64_t res_ld;
   bf16_t* y;
 };
 
@@ -32,14 +37,28 @@ __global__ __launch_bounds__(256) void k_ln_mod(LnArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
-  const float* xr = a.x + row * a.D;
+  float* xr = a.x + row * a.D;
+  const int64_t sr = row / a.rows_per_src;
   f32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = *(const f32x4*)(xr + 4 * (lane + 64 * i));
+  if (a.res_mode) {
+    const bf16_t* rr = a.res + row * a.D;
+    u32x2 rw[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) rw[i] = *(const u32x2*)(rr + 4 * (lane + 64 * i));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = 4 * (lane + 64 * i);
+      f32x4 r = {lo_bf16(rw[i].x), hi_bf16(rw[i].x), lo_bf16(rw[i].y), hi_bf16(rw[i].y)};
+      if (a.res_mode == 2) r *= *(const f32x4*)(a.res_tab + c) + *(const f32x4*)(a.res_src + sr * a.res_ld + c);
+      v[i] += r;
+      *(f32x4*)(xr + c) = v[i];
+    }
+  }
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    v[i] = *(const f32x4*)(xr + 4 * (lane + 64 * i));
-    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
-  }
+  for (int i = 0; i < NV; ++i) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   const float inv_d = 1.0f / (float)a.D;
   const float mean = wave_sum(s) * inv_d;
   float q = 0.f;
@@ -52,7 +71,6 @@ __global__ __launch_bounds__(256) void k_ln_mod(LnArgs a) {
   const float rstd = 1.0f / sqrtf(var + a.eps);
   bf16_t* yr = a.y + row * a.D;
   if (a.mode == 0) {
-    const int64_t sr = row / a.rows_per_src;
     const float* ssh = a.src + sr * a.src_ld + a.src_shift_off;
     const float* ssc = a.src + sr * a.src_ld + a.src_scale_off;
 #pragma unroll
@@ -224,14 +242,15 @@ __global__ void k_sinusoid(const float* __restrict__ t, int64_t rows, int freq_d
 #define NV_CASES(X) X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8) X(9) X(10) X(11) X(12) X(13) X(14) X(15) X(16) \
   X(17) X(18) X(19) X(20) X(21) X(22) X(23) X(24)
 
-hipError_t launch_layernorm(const float* x, int64_t rows, int64_t D, float eps, int mode, const float* tab_shift,
+hipError_t launch_layernorm(float* x, int64_t rows, int64_t D, float eps, int mode, const float* tab_shift,
                             const float* tab_scale, const float* src, int64_t src_ld, int64_t src_shift_off,
                             int64_t src_scale_off, int64_t rows_per_src, const float* gamma, const float* beta,
+                            int res_mode, const bf16_t* res, const float* res_tab, const float* res_src, int64_t res_ld,
                             bf16_t* y, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (D % 256 != 0 || D / 256 > 24) return hipErrorInvalidValue;
   LnArgs a{x, rows, D, eps, mode, tab_shift, tab_scale, src, src_ld, src_shift_off, src_scale_off,
-           rows_per_src > 0 ? rows_per_src : 1, gamma, beta, y};
+           rows_per_src > 0 ? rows_per_src : 1, gamma, beta, res_mode, res, res_tab, res_src, res_ld, y};
   dim3 grid((unsigned)ceil_div(rows, 4)), block(256);
   switch (D / 256) {
 #define X(n) case n: hipLaunchKernelGGL(k_ln_mod<n>, grid, block, 0, s, a); break;

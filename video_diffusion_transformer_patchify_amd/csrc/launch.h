@@ -21,9 +21,10 @@ hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64
 hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, int64_t M,
                            int64_t N, int64_t K, float* C, int64_t ldc, int silu_in, int silu_out, hipStream_t s);
 
-hipError_t launch_layernorm(const float* x, int64_t rows, int64_t D, float eps, int mode, const float* tab_shift,
+hipError_t launch_layernorm(float* x, int64_t rows, int64_t D, float eps, int mode, const float* tab_shift,
                             const float* tab_scale, const float* src, int64_t src_ld, int64_t src_shift_off,
                             int64_t src_scale_off, int64_t rows_per_src, const float* gamma, const float* beta,
+                            int res_mode, const bf16_t* res, const float* res_tab, const float* res_src, int64_t res_ld,
                             bf16_t* y, hipStream_t s);
 hipError_t launch_rms_rope(bf16_t* buf, int64_t ld, int64_t rows, int64_t D, float eps, int64_t off_a,
                            const float* gamma_a, int64_t off_b, const float* gamma_b, const float* rope, int64_t L,

@@ -4,10 +4,14 @@
 // Forward sequence (diffusers WanTransformer3DModel.forward and WanTransformerBlock.forward as printed
 // on the WanPipeline notes page; block order from the Wan2.1 walk-through page, section 5.2):
 //   patchify -> patch-embed GEMM (fp32 residual x) ; sinusoid -> time MLP (fp32) ; text projection
-//   per block: LN1+mod -> QKV GEMM -> QK RMSNorm + RoPE -> V transpose -> attention -> O GEMM (+gate)
-//              LN2 affine -> Q2 GEMM -> RMSNorm ; ctx K/V GEMM -> RMSNorm(k) -> V transpose
-//              -> cross attention -> O2 GEMM (+residual) ; LN3+mod -> FFN1 GEMM (GELU) -> FFN2 GEMM (+gate)
-//   head: LN + (table + temb) modulation -> proj_out GEMM -> unpatchify
+//   per block: [x += gate2 * ffn of the previous block] LN1+mod -> QKV GEMM -> QK RMSNorm + RoPE
+//              -> V transpose -> attention -> O GEMM
+//              [x += gate1 * attn] LN2 affine -> Q2 GEMM -> RMSNorm ; ctx K/V GEMM -> RMSNorm(k)
+//              -> V transpose -> cross attention -> O2 GEMM
+//              [x += cross-attn] LN3+mod -> FFN1 GEMM (GELU) -> FFN2 GEMM
+//   head: [x += gate2 * ffn] LN + (table + temb) modulation -> proj_out GEMM -> unpatchify
+// Each residual add [..] runs inside the LayerNorm kernel that follows it: the branch's last Linear
+// writes bf16 (as the branch outputs are in the bf16 model), and x stays fp32.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -76,7 +80,7 @@ struct wan_dit {
   std::vector<BlockW> blocks;
   float* head_table; bf16_t* w_out; float* b_out;
   // workspace
-  bf16_t *P, *y, *qkv, *vt, *attn, *hbuf, *text_bf, *ctx_h, *ctx, *kv2, *vt2;
+  bf16_t *P, *y, *qkv, *vt, *attn, *br, *hbuf, *text_bf, *ctx_h, *ctx, *kv2, *vt2;
   float *x, *z, *t_s, *t_h, *temb, *tproj, *rope;
   int64_t ldv_max, ldv2_max, rows_max, trows_max;
 };
@@ -205,6 +209,7 @@ void plan_workspace(wan_dit* h, Arena& ar) {
   h->qkv = ar.take<bf16_t>(Mx * 3 * D);
   h->vt = ar.take<bf16_t>(c.max_batch * D * h->ldv_max);
   h->attn = ar.take<bf16_t>(Mx * D);
+  h->br = ar.take<bf16_t>(Mx * D);
   h->hbuf = ar.take<bf16_t>(Mx * Fd);
   h->z = ar.take<float>(Mx * h->n_out);
   h->t_s = ar.take<float>(R * c.freq_dim);
@@ -446,22 +451,25 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
   // 4. rotary tables for this grid
   HIP_TRY(launch_rope_table(h->rope, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, c.rope_theta, s), "rope table");
 
-  // 5. blocks
+  // 5. blocks.  res_* describe the pending residual: the previous block's FFN output and its gate.
+  int res_mode = 0;
+  const float* res_tab = nullptr;
+  const float* res_src = nullptr;
   for (int k = 0; k < c.num_layers; ++k) {
     const BlockW& b = h->blocks[k];
     // self-attention
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 0 * D, b.table + 1 * D, h->tproj, 6 * D, 0 * D, 1 * D,
-                             rows_per_mod, nullptr, nullptr, h->y, s), "norm1");
+                             rows_per_mod, nullptr, nullptr, res_mode, h->br, res_tab, res_src, 6 * D, h->y, s), "norm1");
     HIP_TRY(launch_gemm_bf16(h->y, D, b.wqkv, D, b.bqkv, M, 3 * D, D, EPI_BF16, h->qkv, 3 * D, nullptr, nullptr, 0, 1, s),
             "qkv");
     HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, s),
             "qk norm rope");
     HIP_TRY(launch_transpose_v(h->qkv, 3 * D, 2 * D, B, L, (int)nh, h->vt, ldv, s), "v transpose");
     HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s), "self attention");
-    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_GATE_F32, h->x, D, b.table + 2 * D, h->tproj + 2 * D,
-                             6 * D, rows_per_mod, s), "attn1 out");
-    // cross-attention
-    HIP_TRY(launch_layernorm(h->x, M, D, eps, 1, nullptr, nullptr, nullptr, 0, 0, 0, 1, b.n2w, b.n2b, h->y, s), "norm2");
+    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn1 out");
+    // cross-attention: x += gate1 * attn, then norm2 (affine)
+    HIP_TRY(launch_layernorm(h->x, M, D, eps, 1, nullptr, nullptr, nullptr, 0, 0, 0, rows_per_mod, b.n2w, b.n2b, 2, h->br,
+                             b.table + 2 * D, h->tproj + 2 * D, 6 * D, h->y, s), "norm2");
     bf16_t* q2 = h->qkv;
     HIP_TRY(launch_gemm_bf16(h->y, D, b.wq2, D, b.bq2, M, D, D, EPI_BF16, q2, D, nullptr, nullptr, 0, 1, s), "q2");
     HIP_TRY(launch_rms_rope(q2, D, M, D, eps, 0, b.gq2, 0, nullptr, nullptr, L, 1, 1, 1, dt, dh, dw, s), "q2 norm");
@@ -470,18 +478,20 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
     HIP_TRY(launch_rms_rope(h->kv2, 2 * D, B * Lt, D, eps, 0, b.gk2, 0, nullptr, nullptr, Lt, 1, 1, 1, dt, dh, dw, s), "k2 norm");
     HIP_TRY(launch_transpose_v(h->kv2, 2 * D, D, B, Lt, (int)nh, h->vt2, ldv2, s), "v2 transpose");
     HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, false, s), "cross attention");
-    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_RES_F32, h->x, D, nullptr, nullptr, 0, 1, s), "attn2 out");
-    // feed-forward
+    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn2 out");
+    // feed-forward: x += cross-attn (ungated), then norm3 + modulation
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 3 * D, b.table + 4 * D, h->tproj, 6 * D, 3 * D, 4 * D,
-                             rows_per_mod, nullptr, nullptr, h->y, s), "norm3");
+                             rows_per_mod, nullptr, nullptr, 1, h->br, nullptr, nullptr, 0, h->y, s), "norm3");
     HIP_TRY(launch_gemm_bf16(h->y, D, b.w1, D, b.b1, M, Fd, D, EPI_GELU_BF16, h->hbuf, Fd, nullptr, nullptr, 0, 1, s), "ffn1");
-    HIP_TRY(launch_gemm_bf16(h->hbuf, Fd, b.w2, Fd, b.b2, M, D, Fd, EPI_GATE_F32, h->x, D, b.table + 5 * D, h->tproj + 5 * D,
-                             6 * D, rows_per_mod, s), "ffn2");
+    HIP_TRY(launch_gemm_bf16(h->hbuf, Fd, b.w2, Fd, b.b2, M, D, Fd, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "ffn2");
+    res_mode = 2;
+    res_tab = b.table + 5 * D;
+    res_src = h->tproj + 5 * D;
   }
 
-  // 6. output head
+  // 6. output head: x += gate2 * ffn of the last block, then norm_out + (table + temb) modulation
   HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, h->head_table, h->head_table + D, h->temb, D, 0, 0, rows_per_mod, nullptr,
-                           nullptr, h->y, s), "norm_out");
+                           nullptr, res_mode, h->br, res_tab, res_src, 6 * D, h->y, s), "norm_out");
   HIP_TRY(launch_gemm_bf16(h->y, D, h->w_out, D, h->b_out, M, h->n_out, D, EPI_F32, h->z, h->n_out, nullptr, nullptr, 0, 1, s),
           "proj_out");
   HIP_TRY(launch_unpatchify(h->z, h->n_out, B, c.out_channels, F, Hz, Wz, out->data, out->dtype, s), "unpatchify");
@@ -538,21 +548,28 @@ extern "C" wan_status wan_op_gemm(const void* x, int64_t ldx, const void* w, int
   return WAN_OK;
 }
 
-extern "C" wan_status wan_op_layernorm(const float* x, int64_t rows, int64_t D, float eps, int32_t mode, const float* tab_shift,
+extern "C" wan_status wan_op_layernorm(float* x, int64_t rows, int64_t D, float eps, int32_t mode, const float* tab_shift,
                                        const float* tab_scale, const float* src, int64_t src_ld, int64_t src_shift_off,
                                        int64_t src_scale_off, int64_t rows_per_src, const float* gamma, const float* beta,
-                                       void* y, void* stream) {
+                                       int32_t res_mode, const void* res, const float* res_tab, const float* res_src,
+                                       int64_t res_ld, void* y, void* stream) {
   g_err.clear();
   REQUIRE(rows >= 0 && D % 256 == 0 && D > 0 && D <= 6144, WAN_ERR_SHAPE, "layernorm: D must be a multiple of 256 <= 6144");
   REQUIRE(mode == 0 || mode == 1, WAN_ERR_INVALID_ARG, "layernorm: mode must be 0 or 1");
+  REQUIRE(res_mode >= 0 && res_mode <= 2, WAN_ERR_INVALID_ARG, "layernorm: res_mode must be 0, 1 or 2");
   REQUIRE(x && y, WAN_ERR_INVALID_ARG, "layernorm: NULL pointer");
+  REQUIRE(rows_per_src > 0, WAN_ERR_INVALID_ARG, "layernorm: rows_per_src must be positive");
   if (mode == 0)
-    REQUIRE(tab_shift && tab_scale && src && rows_per_src > 0 && src_ld % 4 == 0 && src_shift_off % 4 == 0 &&
-                src_scale_off % 4 == 0, WAN_ERR_INVALID_ARG, "layernorm: modulation sources missing or misaligned");
+    REQUIRE(tab_shift && tab_scale && src && src_ld % 4 == 0 && src_shift_off % 4 == 0 && src_scale_off % 4 == 0,
+            WAN_ERR_INVALID_ARG, "layernorm: modulation sources missing or misaligned");
   else
     REQUIRE(gamma && beta, WAN_ERR_INVALID_ARG, "layernorm: affine mode needs gamma and beta");
+  if (res_mode) REQUIRE(res, WAN_ERR_INVALID_ARG, "layernorm: residual mode needs the branch output");
+  if (res_mode == 2)
+    REQUIRE(res_tab && res_src && res_ld % 4 == 0, WAN_ERR_INVALID_ARG, "layernorm: gated residual needs res_tab, res_src");
   HIP_TRY(launch_layernorm(x, rows, D, eps, mode, tab_shift, tab_scale, src, src_ld, src_shift_off, src_scale_off, rows_per_src,
-                           gamma, beta, (bf16_t*)y, (hipStream_t)stream), "layernorm");
+                           gamma, beta, res_mode, (const bf16_t*)res, res_tab, res_src, res_ld, (bf16_t*)y,
+                           (hipStream_t)stream), "layernorm");
   return WAN_OK;
 }
 
