@@ -135,6 +135,44 @@ def cpu_baseline(cfg, budget_s: float):
     return est_step, sample_s, threads, nq
 
 
+def probe(cfg):
+    """One launch each of the kernels whose HBM traffic is read from rocprofv3 counters, plus a plain
+    1 GiB device copy (read 1 GiB, write 1 GiB) that calibrates FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    from video_diffusion_transformer_patchify_amd import binding as Bd
+
+    torch.cuda.set_device(0)
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")        # 1 GiB
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    B, L, D, nh, Fd = cfg.batch, cfg.tokens, cfg.dim, cfg.num_heads, cfg.ffn_dim
+    M = B * L
+    g = torch.Generator(device="cuda").manual_seed(0)
+    qkv = torch.randn((M, 3 * D), generator=g, device="cuda").to(torch.bfloat16)
+    ldv = (L + 63) // 64 * 64
+    vt = Bd.op_transpose_v(qkv, 2 * D, B, L, nh, ldv)
+    out = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    Bd.op_attention(qkv, qkv[:, D:], vt, out, B, L, L, nh)
+    torch.cuda.synchronize()
+    x = torch.randn((M, D), generator=g, device="cuda")
+    tab = torch.zeros((6, D), device="cuda")
+    tsrc = torch.zeros((B, 6 * D), device="cuda")
+    Bd.op_layernorm(x, 1e-6, 0, out, tab_shift=tab[0], tab_scale=tab[1], src=tsrc, src_ld=6 * D, src_shift_off=0,
+                    src_scale_off=D, rows_per_src=L)
+    torch.cuda.synchronize()
+    w1 = (torch.randn((Fd, D), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    b1 = torch.zeros(Fd, device="cuda")
+    h = torch.empty((M, Fd), dtype=torch.bfloat16, device="cuda")
+    Bd.op_gemm(out, w1, b1, Bd.EPI_GELU_BF16, h)
+    torch.cuda.synchronize()
+    print("probe done", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,10 +181,16 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (1..5); 2 = Wan2.1-1.3B, 2x32760 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--probe", action="store_true", help="run the counter-calibration kernels only (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
+    if args.probe:
+        from wan_inputs import get_config
+
+        probe(get_config(args.config))
+        return
 
     import numpy as np  # noqa: F401
     import torch

@@ -1,0 +1,67 @@
+"""Write sampled fp64-oracle outputs of the full DiT forward for the large workloads.
+
+The GPU end-to-end tests at full size compare the GPU output at these sampled positions (and the
+output's overall L2 norm) with the oracle.  Inputs and weights are regenerated from the seeded
+generator on both sides, so only the oracle's outputs are stored.  This script calls only the oracle
+and the seeded generator.
+
+usage: python tests/golden/make_forward_golden.py CFG_ID [--layers N] [--samples S] [--workers W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from oracle import wan_oracle as O  # noqa: E402
+from wan_inputs import Weights, draw_inputs, get_config  # noqa: E402
+
+
+def oracle_hash() -> str:
+    with open(os.path.join(ROOT, "oracle", "wan_oracle.py"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def golden_path(cfg_id: int, layers: int) -> str:
+    return os.path.join(HERE, f"forward_cfg{cfg_id}_L{layers}.npz")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("cfg_id", type=int)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--samples", type=int, default=32768)
+    ap.add_argument("--workers", type=int, default=8)
+    args = ap.parse_args()
+    cfg = get_config(args.cfg_id)
+    if args.layers is not None:
+        cfg = cfg.with_layers(args.layers)
+    w = Weights(cfg)
+    lat, t, txt = draw_inputs(cfg)
+    t0 = time.time()
+
+    def drop(prefix):
+        w.drop(prefix)
+        print(f"  {prefix} done at {time.time() - t0:.0f}s", flush=True)
+
+    out = O.forward(cfg, w, lat.f64(), t.f64(), txt.f64(), workers=args.workers, drop=drop)
+    elapsed = time.time() - t0
+    rng = np.random.default_rng(12345)
+    n = out.size
+    idx = np.unique(np.concatenate([rng.integers(0, n, args.samples), np.arange(64), np.arange(n - 64, n)]))
+    np.savez(golden_path(args.cfg_id, cfg.num_layers), index=idx.astype(np.int64), value=out.reshape(-1)[idx],
+             sumsq=np.array([float((out * out).sum())]), shape=np.array(out.shape), seconds=np.array([elapsed]),
+             oracle=np.array([oracle_hash()]))
+    print(f"cfg {args.cfg_id} layers {cfg.num_layers}: {elapsed:.0f}s, |out| = {np.sqrt((out * out).sum()):.4f}", flush=True)
+
+
+if __name__ == "__main__":
+    main()
