@@ -1,0 +1,109 @@
+"""Full-size end-to-end parity of wan_dit_forward against stored fp64-oracle samples.
+
+Each workload runs at its real token count and width (the depth is the stored golden's: all blocks
+where the oracle run finished in reasonable time, otherwise the first blocks of the stack).  The
+goldens hold oracle outputs at a seeded random subset of positions plus the first and last 64, and
+the sum of squares of the whole oracle output; they are written by tests/golden/make_forward_golden.py,
+which calls only the oracle and the seeded generator.
+
+Bars, on the sampled positions: relative L2 <= 2e-2 and max abs <= 5e-2; and the output's whole L2
+norm within 2e-2 of the oracle's (implied by the relative-L2 bar on the full output).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from wan_inputs import Weights, draw_inputs, get_config
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+REL_L2_BAR, MAX_ABS_BAR = 2e-2, 5e-2
+
+
+@pytest.fixture(scope="module")
+def G():
+    import gpu_common
+
+    return gpu_common
+
+
+def golden(cfg_id, layers):
+    path = os.path.join(HERE, "golden", f"forward_cfg{cfg_id}_L{layers}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"no stored oracle output for workload {cfg_id} at {layers} blocks")
+    return np.load(path)
+
+
+def run_forward(G, cfg, reps=1):
+    import torch
+
+    from video_diffusion_transformer_patchify_amd.harness import upload_weights
+
+    w = Weights(cfg)
+    lat, t, txt = draw_inputs(cfg)
+    G.note(f"  uploading {cfg.name} weights ({cfg.num_layers} blocks)")
+    wd = upload_weights(w, threads=16)
+    model = G.B.WanDiT(G.B.make_config(cfg), wd)
+    del wd
+    torch.cuda.empty_cache()
+    args = (G.to_device(lat), G.to_device(t), G.to_device(txt))
+    outs = []
+    for _ in range(reps):
+        G.note(f"  forward {cfg.name} tokens={cfg.tokens} batch={cfg.batch}")
+        outs.append(model.forward(*args))
+        torch.cuda.synchronize()
+    model.close()
+    return outs
+
+
+def check_against_golden(G, out, g):
+    got = G.to_f64(out)
+    assert tuple(got.shape) == tuple(int(s) for s in g["shape"])
+    flat = got.reshape(-1)
+    idx, ref = g["index"], g["value"]
+    r = G.rel_l2(flat[idx], ref)
+    m = G.max_abs(flat[idx], ref)
+    norm_ratio = float(np.sqrt((got * got).sum() / g["sumsq"][0]))
+    print(f"samples={idx.size} rel_l2={r:.3e} max_abs={m:.3e} norm_ratio={norm_ratio:.5f} "
+          f"oracle={g['oracle'][0]}", flush=True)
+    assert np.isfinite(got).all()
+    assert r <= REL_L2_BAR and m <= MAX_ABS_BAR, (r, m)
+    assert abs(norm_ratio - 1.0) <= REL_L2_BAR, norm_ratio
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg_id,layers", [
+    (2, None),      # Wan2.1-1.3B geometry, CFG batch 2, 32760 tokens, all 30 blocks
+    (3, None),      # I2V block stack, 36 channels, D=5120, 7920 tokens, all 4 blocks
+    (4, None),      # TI2V-5B geometry, per-token timesteps, 27280 tokens, all 30 blocks
+    (4, 2),         # the same workload, first 2 blocks
+    (5, 1),         # Wan-14B geometry at 720p, 75600 tokens, first block
+])
+def test_full_size_vs_oracle(G, cfg_id, layers):
+    cfg = get_config(cfg_id)
+    if layers is not None:
+        cfg = cfg.with_layers(layers)
+    g = golden(cfg_id, cfg.num_layers)
+    G.note(f"full-size forward {cfg.name} blocks={cfg.num_layers}")
+    (out,) = run_forward(G, cfg)
+    check_against_golden(G, out, g)
+
+
+@pytest.mark.timeout(900)
+def test_largest_workload_all_blocks_deterministic(G):
+    """Wan-14B geometry at 720p with all 40 blocks (the largest workload): finite, the expected shape,
+    bit-identical on a second run, and an output RMS within broad bounds (the oracle's one-block output
+    of this workload has RMS of order 1)."""
+    cfg = get_config(5)
+    G.note("largest workload, all blocks, twice")
+    out1, out2 = run_forward(G, cfg, reps=2)
+    assert tuple(out1.shape) == cfg.out_shape
+    b1, b2 = G.bf16_bits(out1), G.bf16_bits(out2)
+    assert np.array_equal(b1, b2)
+    got = G.to_f64(out1)
+    assert np.isfinite(got).all()
+    rms = float(np.sqrt((got * got).mean()))
+    print(f"rms={rms:.4f}", flush=True)
+    assert 0.05 < rms < 50.0

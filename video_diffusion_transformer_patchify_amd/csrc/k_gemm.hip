@@ -13,6 +13,8 @@
 //   EPI_F32        out_f32  = acc + bias                                  (patch embed, proj_out)
 //   EPI_RES_F32    out_f32 += acc + bias
 //   EPI_GATE_F32   out_f32 += (acc + bias) * (gate_tab[n] + gate_src[row(m)][n])
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -193,102 +195,238 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------------
-// Large-problem kernel: 256 x 256 x 64 tiles, 4 waves of 128 x 128, operands copied global -> LDS with
-// gfx950's direct loads (global_load_lds_dwordx4: lane l of an instruction fills bytes 16 l .. 16 l + 15
-// of a 1 KB LDS block), double buffered, no register staging.  Each 128-byte LDS row (64 bf16 of K)
-// holds its eight 16-byte chunks XOR-swizzled by swz(row) so fragment reads are free of bank
-// conflicts; the swizzle is applied by choosing which global chunk each lane fetches.  Tiles are
-// visited in groups of GROUP_M tile rows so the tiles that run together on one XCD share A rows and
-// B columns in its L2.
+// Large-problem kernel, persistent: 256 x 256 output tiles, 4 waves of 128 x 128, K in stages of 32.
+//  * One workgroup per CU (160 KB of LDS: four 32 KB operand stages and a 32 KB epilogue buffer) walks
+//    a contiguous range of its XCD's tiles in grouped order (GROUP_M tile rows at a time), so the
+//    tiles that run together on one XCD share X rows and W rows in its L2.
+//  * Operands go global -> LDS with gfx950's direct loads (global_load_lds_dwordx4: lane l of one
+//    instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), three to four stages ahead of
+//    use.  The 8 direct loads of a stage sit between the MFMAs, one per 4, and the barrier waits only
+//    for the stage about to be read, never for the whole queue.
+//  * Each 64-byte LDS row (32 bf16 of K) holds its four 16-byte chunks XOR-swizzled by swz(row) so
+//    fragment reads are free of bank conflicts; the swizzle is applied by choosing which global chunk
+//    each lane fetches.
+//  * The next tile's first stages are requested before the epilogue so their latency hides behind
+//    it; bf16 epilogues pass through LDS and leave as whole 256-byte row segments.
 // ---------------------------------------------------------------------------------------------------
 constexpr int BIG = 256;
 constexpr int GROUP_M = 8;
-constexpr int OPND_BYTES = BIG * BK * 2;        // one operand tile, 32 KB
-constexpr int STAGE_BYTES = 2 * OPND_BYTES;     // X tile then W tile
+constexpr int BK4 = 32;                          // K per stage
+constexpr int NSTAGE = 4;
+constexpr int OPND_BYTES = BIG * BK4 * 2;        // one operand tile, 16 KB
+constexpr int STAGE_BYTES = 2 * OPND_BYTES;      // X tile then W tile
+constexpr int EPI_SLICE = 32 * 128 * 2;          // per-wave epilogue buffer: 32 rows x 128 bf16
+constexpr int SLOTS_PER_XCD = 32;                // CUs per XCD: one persistent workgroup each
 
-__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
+__device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
+// bf16 epilogue of one wave's 128 x 128 block through its LDS slice, 32 rows at a time.  Writes: lane
+// (l32, g) puts its 4 values of chunk c (= 8 output columns) of row l32 into 16-byte position
+// c ^ (l32 & 15), 8-byte half g ^ (l32 >> 4) (conflict-free); reads: 16 lanes per row take the row's
+// 16 chunks, so each store instruction writes 4 whole 256-byte row segments.
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds[2][STAGE_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-
-  // ---- tile order: XCD-contiguous ranges, grouped by GROUP_M tile rows
-  const int nb = a.tiles_m * a.tiles_n;
-  const int tile = xcd_remap(blockIdx.x, nb);
-  const int width = GROUP_M * a.tiles_n;
-  const int first_m = (tile / width) * GROUP_M;
-  const int gsz = min(a.tiles_m - first_m, GROUP_M);
-  const int tm = first_m + (tile % width) % gsz;
-  const int tn = (tile % width) / gsz;
-  const int64_t m0 = (int64_t)tm * BIG, n0 = (int64_t)tn * BIG;
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
-
-  // ---- direct-load addressing: instruction I = 8 wave + i covers tile rows 8 I .. 8 I + 7;
-  //      lane -> row 8 I + lane / 8, LDS chunk position lane % 8, global chunk (lane % 8) ^ swz(row).
-  uint32_t xo[8], wo[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (8 * wave + i) + (lane >> 3);
-    const int cchunk = (lane & 7) ^ row_swz(r);
-    int64_t rx = m0 + r, rw = n0 + r;
-    if (rx > a.M - 1) rx = a.M - 1;        // rows past the end repeat the last row (never stored)
-    if (rw > a.N - 1) rw = a.N - 1;
-    xo[i] = (uint32_t)(((rx - m0) * a.ldx + cchunk * 8) * 2);
-    wo[i] = (uint32_t)(((rw - n0) * a.ldw + cchunk * 8) * 2);
-  }
-  const char* xt = (const char*)(a.x + m0 * a.ldx);
-  const char* wt = (const char*)(a.w + n0 * a.ldw);
-  auto issue = [&](int kt, int buf) {
-    char* lx = lds[buf];
-    char* lw = lds[buf] + OPND_BYTES;
-    const int kb = kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(xt + kb + xo[i]), (lds_void*)(lx + (8 * wave + i) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(wt + kb + wo[i]), (lds_void*)(lw + (8 * wave + i) * 1024), 16, 0, 0);
-  };
-
-  // ---- fragment read offsets: rows (multiples of 32) + l32 share the swizzle of l32
-  int foff[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) foff[ks] = l32 * 128 + (((2 * ks + g) ^ row_swz(l32)) << 4);
-
-  f32x16 acc[4][4];
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[4][4], int64_t mb, int64_t nb,
+                                               char* slice, int lane, int l32, int g) {
+  f32x4 bias[4][4];
+  const bool full_n = nb + 128 <= a.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
-
-  const int nk = (int)(a.K / BK);
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue(kt + 1, buf ^ 1);
-    const char* lx = lds[buf] + wm0 * 128;
-    const char* lw = lds[buf] + OPND_BYTES + wn0 * 128;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const u32x4*)(lw + i * 32 * 128 + foff[ks]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *(const u32x4*)(lx + j * 32 * 128 + foff[ks]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j], 0, 0, 0);
+    for (int rg = 0; rg < 4; ++rg) {
+      int64_t n = nb + 32 * i + 8 * rg + 4 * g;
+      if (!full_n && n >= a.N) n = a.N - 4;
+      bias[i][rg] = *(const f32x4*)(a.bias + n);
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  const int wrow = l32 * 256 + 8 * (g ^ (l32 >> 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
+        v += bias[i][rg];
+        if constexpr (EPI == EPI_GELU_BF16) {
+          v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+        }
+        u32x2 o;
+        o.x = pack_bf16x2(v.x, v.y);
+        o.y = pack_bf16x2(v.z, v.w);
+        const int c = 4 * i + rg;
+        *(u32x2*)(slice + wrow + ((c ^ (l32 & 15)) << 4)) = o;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slice is written before any lane reads it
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int row = 4 * s + (lane >> 4), c = lane & 15;
+      u32x4 d = *(const u32x4*)(slice + row * 256 + ((c ^ (row & 15)) << 4));
+      if (row >> 4) d = (u32x4){d.z, d.w, d.x, d.y};
+      const int64_t m = mb + 32 * j + row, n = nb + 8 * c;
+      if (m < a.M && (full_n || n < a.N)) *(u32x4*)((bf16_t*)a.out + m * a.ldo + n) = d;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): reads done before the next slab overwrites
+    __builtin_amdgcn_wave_barrier();
   }
-  store_tile<EPI, 4, 4>(a, acc, m0 + wm0, n0 + wn0, l32, g);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES + 4 * EPI_SLICE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+
+  // ---- this workgroup's tiles: XCD blockIdx % 8 owns tiles [lo, hi) of the grouped order; its
+  //      SLOTS_PER_XCD workgroups take every SLOTS_PER_XCD-th one
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int per = (ntiles + 7) / 8;
+  const int lo = (blockIdx.x % 8) * per;
+  const int hi = min(ntiles, lo + per);
+  int t = lo + (int)(blockIdx.x / 8);
+  if (t >= hi) return;
+
+  int64_t m0, n0;
+  uint32_t xo[4], wo[4];
+  const char* xt;
+  const char* wt;
+  // tile t: origin, and per-lane direct-load offsets.  Instruction I = 4 wave + i covers tile rows
+  // 16 I .. 16 I + 15: lane -> row 16 I + lane / 4, LDS chunk lane % 4, global chunk (lane % 4) ^ swz(row).
+  // Rows past M or N repeat the last row (their results are never stored).
+  auto setup = [&](int tt) {
+    const int width = GROUP_M * a.tiles_n;
+    const int first_m = (tt / width) * GROUP_M;
+    const int gsz = min(a.tiles_m - first_m, GROUP_M);
+    const int tm = first_m + (tt % width) % gsz;
+    const int tn = (tt % width) / gsz;
+    m0 = (int64_t)tm * BIG;
+    n0 = (int64_t)tn * BIG;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * (4 * wave + i) + (lane >> 2);
+      const int cchunk = (lane & 3) ^ row_swz(r);
+      int64_t rx = m0 + r, rw = n0 + r;
+      if (rx > a.M - 1) rx = a.M - 1;
+      if (rw > a.N - 1) rw = a.N - 1;
+      xo[i] = (uint32_t)(((rx - m0) * a.ldx + cchunk * 8) * 2);
+      wo[i] = (uint32_t)(((rw - n0) * a.ldw + cchunk * 8) * 2);
+    }
+    xt = (const char*)(a.x + m0 * a.ldx);
+    wt = (const char*)(a.w + n0 * a.ldw);
+  };
+  // instruction i of half h of stage kt: h = 0 the X tile, h = 1 the W tile
+  auto dma = [&](int kt, int h, int i) {
+    char* dst = lds + (kt % NSTAGE) * STAGE_BYTES + h * OPND_BYTES + (4 * wave + i) * 1024;
+    const char* src = (h ? wt + wo[i] : xt + xo[i]) + kt * BK4 * 2;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+  };
+  // stages 0..2 whole and the first half of stage 3 (28 instructions)
+  auto prologue = [&]() {
+#pragma unroll
+    for (int st = 0; st < 3; ++st)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma(st, h, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma(3, 0, i);
+  };
+
+  int foff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) foff[ks] = l32 * 64 + (((2 * ks + g) ^ row_swz(l32)) << 4);
+
+  f32x16 acc[4][4];
+  u32x4 fa[2][4], fb[2][4];
+  // fragment q (0..7) of k-substep ks of stage kt: q < 4 -> W rows wn0 + 32 q, else X rows
+  auto frag = [&](int kt, int ks, int q) {
+    const char* base = lds + (kt % NSTAGE) * STAGE_BYTES;
+    if (q < 4) fa[ks][q] = *(const u32x4*)(base + OPND_BYTES + (wn0 + q * 32) * 64 + foff[ks]);
+    else fb[ks][q - 4] = *(const u32x4*)(base + (wm0 + (q - 4) * 32) * 64 + foff[ks]);
+  };
+  auto mma = [&](int ks, int q) {     // MFMAs 2q, 2q+1 of k-substep ks
+    const int i = q >> 1, j0 = 2 * (q & 1);
+    acc[i][j0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[ks][i]), as_bf16x8(fb[ks][j0]), acc[i][j0], 0, 0, 0);
+    acc[i][j0 + 1] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa[ks][i]), as_bf16x8(fb[ks][j0 + 1]), acc[i][j0 + 1], 0, 0, 0);
+  };
+  // One K step kt in two phases of 16 MFMAs, every 2 MFMAs followed by one fragment read and every 4 by
+  // one direct load (sched_barrier keeps this order):
+  //   A: MFMAs of substep 0 | fragments of substep 1 | second half of stage kt+3
+  //   own part of stage kt+1 landed, every fragment read of stage kt returned, workgroup barrier
+  //   B: MFMAs of substep 1 | substep-0 fragments of stage kt+1 | first half of stage kt+4, which goes
+  //      into stage kt's buffer (free once every wave has passed the barrier)
+  // WAIT = stages allowed in flight at the barrier (8 instructions each).
+  auto step = [&](int kt, auto issue_a, auto issue_b, auto wait_n, auto next) {
+    constexpr bool IA = decltype(issue_a)::value, IB = decltype(issue_b)::value;
+    constexpr bool NEXT = decltype(next)::value;
+    constexpr int WAIT = decltype(wait_n)::value;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mma(0, q);
+      frag(kt, 1, q);
+      if (IA && (q & 1)) dma(kt + 3, 1, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NEXT) {
+      if constexpr (WAIT == 2) __builtin_amdgcn_s_waitcnt(0x4070);        // vmcnt(16) lgkmcnt(0)
+      else if constexpr (WAIT == 1) __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0x0070);                            // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mma(1, q);
+      if (NEXT) frag(kt + 1, 0, q);
+      if (IB && (q & 1)) dma(kt + 4, 0, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  using W2 = std::integral_constant<int, 2>;
+  using W1 = std::integral_constant<int, 1>;
+  using W0 = std::integral_constant<int, 0>;
+  const int nk = (int)(a.K / BK4);       // >= 4 (checked by the launcher)
+  char* slice = lds + NSTAGE * STAGE_BYTES + wave * EPI_SLICE;
+
+  setup(t);
+  prologue();
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    // stage 0 landed.  Outstanding: this tile's 28 direct loads, and possibly the previous tile's
+    // epilogue stores (or loads issued after the 28).  Loads complete in order, so once at most 20
+    // operations remain, the first 8 loads (stage 0) are done whatever the stores did.
+    __builtin_amdgcn_s_waitcnt(0x4F74);   // vmcnt(20)
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) frag(0, 0, q);
+    int kt = 0;
+    for (; kt + 4 < nk; ++kt) step(kt, T{}, T{}, W2{}, T{});
+    step(kt, T{}, F{}, W2{}, T{});
+    step(kt + 1, F{}, F{}, W1{}, T{});
+    step(kt + 2, F{}, F{}, W0{}, T{});
+    step(kt + 3, F{}, F{}, W0{}, F{});
+    const int64_t tm0 = m0, tn0 = n0;
+    const int tnext = t + SLOTS_PER_XCD;
+    const bool more = tnext < hi;
+    // every wave has read its last fragments before any wave refills the stages
+    __builtin_amdgcn_s_barrier();
+    if (more) {
+      setup(tnext);
+      prologue();
+    }
+    if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16)
+      store_tile_lds<EPI>(a, acc, tm0 + wm0, tn0 + wn0, slice, lane, l32, g);
+    else
+      store_tile<EPI, 4, 4>(a, acc, tm0 + wm0, tn0 + wn0, l32, g);
+    if (!more) break;
+    t = tnext;
+  }
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -310,7 +448,7 @@ hipError_t launch_tile(int epi, GemmArgs& a, hipStream_t s) {
 hipError_t launch_big(int epi, GemmArgs& a, hipStream_t s) {
   a.tiles_m = (int)ceil_div(a.M, BIG);
   a.tiles_n = (int)ceil_div(a.N, BIG);
-  dim3 grid(a.tiles_m * a.tiles_n), block(256);
+  dim3 grid(8 * SLOTS_PER_XCD), block(256);
   switch (epi) {
     case EPI_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_BF16>, grid, block, 0, s, a); break;
     case EPI_GELU_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_GELU_BF16>, grid, block, 0, s, a); break;
@@ -388,9 +526,12 @@ hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64
   a.rows_per_gate = rows_per_gate > 0 ? rows_per_gate : 1;
   // Large problems: 256x256 tiles with direct LDS loads.  Small ones: 128x128 so the grid still covers
   // the chip.  The direct-load offsets are 32-bit: 256 rows of the larger leading dimension must fit.
+  // The persistent kernel also needs 4+ K stages of 32 and, for its 16-byte bf16 stores, N, ldo and
+  // the output address aligned to 8 elements.
   const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
   const bool offsets_fit = 256 * (ldx > ldw ? ldx : ldw) * 2 < (1LL << 31);
-  if (big_tiles >= 512 && offsets_fit) return launch_big(epi, a, s);
+  const bool aligned = N % 8 == 0 && ldo % 8 == 0 && ((uintptr_t)out & 15) == 0;
+  if (big_tiles >= 512 && offsets_fit && K % 32 == 0 && K >= 128 && aligned) return launch_big(epi, a, s);
   return launch_tile<128, 128, 64, 64>(epi, a, s);
 }
 
