@@ -29,6 +29,15 @@ WAN_DEV uint32_t pack_bf16x2(float a, float b) {
 WAN_DEV float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 WAN_DEV float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Workgroup barrier without the memory fence of __syncthreads (which makes the compiler wait for every
+// outstanding global access, direct-to-LDS loads included): callers wait for what they need with
+// s_waitcnt first.  The empty asm statements keep the compiler from moving memory accesses across.
+WAN_DEV void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 WAN_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Wave-wide (64 lanes) reductions.

@@ -236,28 +236,32 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     v_off[i] = (uint32_t)(((int64_t)v_row * a.ldv + v_col) * 2);
   }
   const bool tail_rows = (a.Lkv % KT) != 0;
-  auto issue = [&](int t) {
+  // half 0 of tile t: its 4 K instructions; half 1: its 4 V instructions
+  auto issue = [&](int t, int part) {
     const int64_t key0 = (int64_t)t * KT;
     char* lk = lds[t % NBUF];
-    char* lv = lk + K_TILE_BYTES;
-    const char* kt = (const char*)(kbase + key0 * a.ldk);
-    const char* vtb = (const char*)(vbase + key0);
-    if (tail_rows && t == n_tiles - 1) {
-      // last, partial tile: rows past the end re-read the last valid row (their scores are masked)
+    if (part == 0) {
+      const char* kt = (const char*)(kbase + key0 * a.ldk);
+      if (tail_rows && t == n_tiles - 1) {
+        // last, partial tile: rows past the end re-read the last valid row (their scores are masked)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = key0 + k_row[i] < a.Lkv ? k_row[i] : a.Lkv - 1 - key0;
-        const uint32_t off = (uint32_t)(k_off[i] + (key - k_row[i]) * a.ldk * 2);
-        __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t key = key0 + k_row[i] < a.Lkv ? k_row[i] : a.Lkv - 1 - key0;
+          const uint32_t off = (uint32_t)(k_off[i] + (key - k_row[i]) * a.ldk * 2);
+          __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(kt + k_off[i]), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
       }
     } else {
+      const char* vtb = (const char*)(vbase + key0);
+      char* lv = lk + K_TILE_BYTES;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(kt + k_off[i]), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(vtb + v_off[i]), (lds_void*)(lv + (4 * wave + i) * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(vtb + v_off[i]), (lds_void*)(lv + (4 * wave + i) * 1024), 16, 0, 0);
   };
 
   AttnState st;
@@ -272,11 +276,17 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   const float grow_thr = RESCALE_LOG2 / c;   // raw-score margin before the max is raised
   const int last_lim = (int)(a.Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
 
-  // ---- prologue: tiles 0 and 1 resident, scores and max of sub-tile 0
-  issue(0);
-  if (n_tiles > 1) issue(1);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // ---- prologue: tiles 0 and 1 requested, tile 0 resident; scores and max of sub-tile 0
+  issue(0, 0);
+  issue(0, 1);
+  if (n_tiles > 1) {
+    issue(1, 0);
+    issue(1, 1);
+    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): own part of tile 0 landed (loads complete in order)
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  }
+  block_sync();
   f32x16 s_cur[2], s_next[2];
   float mx[2];
   scores(s_cur, qf, lds[0], 0, l32, g);
@@ -285,10 +295,13 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   maybe_rescale(st, mx, c, grow_thr);
 
   // One pipelined step: S(j+1) with P(j); PV(j) with max(S(j+1)).  LAST: S(j+1) is the final sub-tile.
+  // Tile t+2 is requested during tile t (K in its first half, V in its second) into the buffer of tile
+  // t-1, which every wave finished reading before the barrier that ended tile t-1.  The barrier that
+  // ends tile t waits only for tile t+1.
   auto step = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int t = j >> 1, half = j & 1;
-    if (!half && t + 2 < n_tiles) issue(t + 2);
+    if (t + 2 < n_tiles) issue(t + 2, half);
     u32x4 pf[2][2];
     scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
     probs(st, s_cur, pf, c);
@@ -299,8 +312,9 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     row_max(s_next, mx);
     maybe_rescale(st, mx, c, grow_thr);
     if (half) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      if (t + 2 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) lgkmcnt(0): tile t+1 landed
+      else __builtin_amdgcn_s_waitcnt(0x0070);                   // vmcnt(0) lgkmcnt(0)
+      block_sync();
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) s_cur[qb] = s_next[qb];
@@ -355,3 +369,4 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
   else hipLaunchKernelGGL(k_flash_attn<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+

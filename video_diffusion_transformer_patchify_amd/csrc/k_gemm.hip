@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
       if constexpr (WAIT == 2) __builtin_amdgcn_s_waitcnt(0x4070);        // vmcnt(16) lgkmcnt(0)
       else if constexpr (WAIT == 1) __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) lgkmcnt(0)
       else __builtin_amdgcn_s_waitcnt(0x0070);                            // vmcnt(0) lgkmcnt(0)
-      __builtin_amdgcn_s_barrier();
+      block_sync();
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     // epilogue stores (or loads issued after the 28).  Loads complete in order, so once at most 20
     // operations remain, the first 8 loads (stage 0) are done whatever the stores did.
     __builtin_amdgcn_s_waitcnt(0x4F74);   // vmcnt(20)
-    __builtin_amdgcn_s_barrier();
+    block_sync();
 #pragma unroll
     for (int q = 0; q < 8; ++q) frag(0, 0, q);
     int kt = 0;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     const int tnext = t + SLOTS_PER_XCD;
     const bool more = tnext < hi;
     // every wave has read its last fragments before any wave refills the stages
-    __builtin_amdgcn_s_barrier();
+    block_sync();
     if (more) {
       setup(tnext);
       prologue();
