@@ -216,16 +216,17 @@ def main():
     for _ in range(args.warmup):
         model.forward(latent, ts, text, out, stream=stream)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
+    evs[0].record(stream)
     for i in range(args.steps):
         model.forward(latent, ts, text, out, stream=stream)
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     print(f"# timed {args.steps} steps: {ms:.2f} ms/step (wall {wall * 1e3 / args.steps:.2f})", file=sys.stderr, flush=True)
     assert torch.isfinite(out.float()).all().item(), "non-finite output"
 
@@ -237,6 +238,11 @@ def main():
     attn_flops = 4 * cfg.batch * cfg.tokens * cfg.tokens * cfg.dim
     attn_tf = attn_flops / (attn_ms * 1e-3) / 1e12
     print(f"# self-attention kernel {attn_ms:.3f} ms/launch = {attn_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    # measured dense bf16 MFMA ceiling on this device (MFMA-only probe kernel, no memory traffic)
+    peak_zero = Bd.probe_mfma(random_operands=False, stream=stream)
+    peak_rand = Bd.probe_mfma(random_operands=True, stream=stream)
+    print(f"# MFMA probe: {peak_zero:.0f} TFLOP/s on zero operands, {peak_rand:.0f} on random bf16 operands",
+          file=sys.stderr, flush=True)
     model.close()
     del latent, text, out
     torch.cuda.empty_cache()
@@ -249,6 +255,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 3),
+        "ms_per_step_min": round(per_step[0], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -259,6 +267,9 @@ def main():
                                f"text {cfg.text_len}x{cfg.text_dim}",
                    "global_batch": cfg.batch, "seq_len": cfg.tokens, "parallelism": "single GPU"},
         "mfma_frac_end_to_end": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "mfma_peak_measured": {"zero_operands": round(peak_zero, 1), "random_operands": round(peak_rand, 1),
+                               "unit": "TFLOP/s", "kernel": "wan_probe_mfma (GEMM inner loop from LDS, 32x32x16 bf16)"},
+        "mfma_frac_of_measured_random": round(tflops / peak_rand, 4),
         "flops_per_step": fl["total"],
         "roofline": {"kernel": "k_flash_attn<self> (self-attention)", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),

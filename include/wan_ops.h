@@ -105,6 +105,15 @@ wan_status wan_op_time_embed(const float* t, int64_t rows, int32_t freq_dim, int
                              const float* b1, const float* w2, const float* b2, const float* wp, const float* bp,
                              float* temb, float* tproj, float* work, void* stream);
 
+/* Measurement aid, not a step of the forward: the dense bf16 MFMA ceiling that the forward's MFMA
+ * fractions are read against.  `blocks` workgroups of 256 threads each run `rounds` rounds of 64
+ * 32x32x16 bf16 MFMAs per wave (16 independent accumulators) on operands held in LDS, with no global
+ * memory traffic; the work is blocks * 4 * rounds * 64 * 32768 FLOP.  random_operands = 0 uses zeros (least power drawn); 1 uses
+ * values drawn like the GEMM operands (U(-1,1) and U(-0.05,0.05)), which shows what dense bf16 work
+ * sustains once the clock settles.  sink: device fp32 [blocks * 256], receives per-thread sums (keeps the
+ * work alive).  Time it with events on `stream`. */
+wan_status wan_probe_mfma(float* sink, int32_t blocks, int64_t rounds, int32_t random_operands, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -385,3 +385,22 @@ def test_layernorm_with_residual(G, rows, D, res_mode, per_token):
     ref = O.layer_norm(x_ref, 1e-6) * (1.0 + tab_t.f64()[1] + s[:, D:2 * D]) + tab_t.f64()[0] + s[:, :D]
     got = G.to_f64(y)
     assert G.rel_l2(got, ref) < 3e-3
+
+
+def test_mfma_probe(G):
+    """The MFMA throughput probe runs, zero operands give exactly zero sums, random ones finite sums, and
+    the measured rate is plausible for one device (below 3 PFLOP/s, above 100 TFLOP/s)."""
+    import torch
+
+    G.note("mfma probe")
+    sink = torch.full((64 * 256,), float("nan"), dtype=torch.float32, device="cuda")
+    assert G.B._probe_mfma(sink.data_ptr(), 64, 8, 0, G.B._stream(None)) == 0
+    G.sync()
+    assert torch.count_nonzero(sink).item() == 0
+    assert G.B._probe_mfma(sink.data_ptr(), 64, 8, 1, G.B._stream(None)) == 0
+    G.sync()
+    assert torch.isfinite(sink).all().item() and torch.count_nonzero(sink).item() > 0
+    tf = G.B.probe_mfma(blocks=256, rounds=50, random_operands=True, reps=1)
+    assert 100.0 < tf < 3000.0, tf
+    with pytest.raises(G.B.WanError):
+        G.B._check(G.B._probe_mfma(sink.data_ptr(), 0, 8, 0, G.B._stream(None)))

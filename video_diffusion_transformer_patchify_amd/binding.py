@@ -76,11 +76,12 @@ _op_qk_norm_rope = _sig("wan_op_qk_norm_rope", [_vp, _i64, _i64, _i64, _f32, _i6
 _op_transpose_v = _sig("wan_op_transpose_v", [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp])
 _op_attention = _sig("wan_op_attention", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp])
 _op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
+_probe_mfma = _sig("wan_probe_mfma", [_vp, _i32, _i64, _i32, _vp])
 
 EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
             "wan_op_patchify", "wan_op_unpatchify", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
-            "wan_op_time_embed"]
+            "wan_op_time_embed", "wan_probe_mfma"]
 
 
 def last_error() -> str:
@@ -269,3 +270,21 @@ def op_time_embed(t: torch.Tensor, freq_dim: int, d: int, w1, b1, w2, b2, wp, bp
                           wp.data_ptr(), bp.data_ptr(), temb.data_ptr(), tproj.data_ptr(), work.data_ptr(),
                           _stream(stream)))
     return temb, tproj
+
+
+def probe_mfma(blocks: int = 1024, rounds: int = 1000, random_operands: bool = True, reps: int = 3, stream=None) -> float:
+    """Dense bf16 MFMA throughput (TFLOP/s) of the probe kernel: best of `reps` timed launches after one
+    warm-up, HIP events on the stream it runs on."""
+    s = stream or torch.cuda.current_stream()
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * rounds * 64 * 32768
+    best = 0.0
+    for i in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        _check(_probe_mfma(sink.data_ptr(), blocks, rounds, int(random_operands), _stream(s)))
+        e1.record(s)
+        e1.synchronize()
+        if i:
+            best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libwan_dit.so")
 
-SOURCES = ["k_patch.hip", "k_gemm.hip", "k_norm.hip", "k_attn.hip", "wan_dit.hip"]
+SOURCES = ["k_patch.hip", "k_gemm.hip", "k_norm.hip", "k_attn.hip", "k_probe.hip", "wan_dit.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -38,3 +38,5 @@ hipError_t launch_sinusoid(const float* t, int64_t rows, int freq_dim, float* ou
 hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
                             bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, bool self_attn,
                             hipStream_t s);
+
+hipError_t launch_mfma_probe(float* sink, int blocks, int64_t rounds, int random_operands, hipStream_t s);

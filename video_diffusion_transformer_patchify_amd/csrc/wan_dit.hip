@@ -648,3 +648,12 @@ extern "C" wan_status wan_op_time_embed(const float* t, int64_t rows, int32_t fr
   HIP_TRY(launch_gemm_f32(temb, D, wp, D, bp, rows, 6 * D, D, tproj, 6 * D, 1, 0, s), "time_proj");
   return WAN_OK;
 }
+
+extern "C" wan_status wan_probe_mfma(float* sink, int32_t blocks, int64_t rounds, int32_t random_operands,
+                                     void* stream) {
+  g_err.clear();
+  REQUIRE(blocks > 0 && rounds > 0, WAN_ERR_SHAPE, "probe_mfma: blocks and rounds must be positive");
+  REQUIRE(sink, WAN_ERR_INVALID_ARG, "probe_mfma: NULL sink");
+  HIP_TRY(launch_mfma_probe(sink, blocks, rounds, random_operands, (hipStream_t)stream), "mfma probe");
+  return WAN_OK;
+}
