@@ -513,6 +513,93 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A, i
   }
 }
 
+// fp32 GEMM on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation), used
+// for the timestep MLP when K is a multiple of 16.  128x128 workgroup tile, 4 waves of 64x64 (2x2 MFMA
+// tiles), K in steps of 16 staged through registers into LDS rows padded to 17 floats (a column read by
+// 32 consecutive rows then touches 32 distinct banks), double buffered.  SiLU of the input is applied on
+// the way into LDS, bias and SiLU of the output in the epilogue.  Rows and columns past M and N load as
+// zero and are not stored.
+constexpr int F_TILE = 128, F_BK = 16, F_LD = F_BK + 1;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_f32m(const float* __restrict__ A, int64_t lda,
+                                                      const float* __restrict__ W, int64_t ldw,
+                                                      const float* __restrict__ bias, int64_t M, int64_t N, int64_t K,
+                                                      float* __restrict__ C, int64_t ldc, int silu_in, int silu_out,
+                                                      int tiles_n) {
+  __shared__ float la[2][F_TILE * F_LD];
+  __shared__ float lw[2][F_TILE * F_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, g = lane >> 5;
+  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * F_TILE, n0 = (int64_t)(blockIdx.x % tiles_n) * F_TILE;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  // staging: thread -> row tid / 2 of each tile, 8 consecutive k at (tid % 2) * 8
+  const int sr = tid >> 1, sk = (tid & 1) * 8;
+  const bool a_ok = m0 + sr < M, w_ok = n0 + sr < N;
+  const float* ap = A + (a_ok ? m0 + sr : 0) * lda + sk;
+  const float* wp = W + (w_ok ? n0 + sr : 0) * ldw + sk;
+  f32x4 ra[2], rw[2];
+  auto load = [&](int64_t k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ra[h] = a_ok ? *(const f32x4*)(ap + k0 + 4 * h) : (f32x4){};
+      rw[h] = w_ok ? *(const f32x4*)(wp + k0 + 4 * h) : (f32x4){};
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float av = ra[h][e];
+        la[buf][sr * F_LD + sk + 4 * h + e] = silu_in ? silu_f(av) : av;
+        lw[buf][sr * F_LD + sk + 4 * h + e] = rw[h][e];
+      }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+  const int nk = (int)(K / F_BK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) load((int64_t)(kt + 1) * F_BK);
+#pragma unroll
+    for (int kk = 0; kk < F_BK / 2; ++kk) {
+      // A operand: output row (wm + 32 i + l32), k = 2 kk + g;  B operand: output column (wn + 32 j + l32)
+      float fa[2], fw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = la[buf][(wm + 32 * i + l32) * F_LD + 2 * kk + g];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fw[j] = lw[buf][(wn + 32 * j + l32) * F_LD + 2 * kk + g];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fw[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+  // acc[i][j] element r: row wm + 32 i + 8 (r/4) + 4 g + r%4, column wn + 32 j + l32
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = n0 + wn + 32 * j + l32;
+    if (n >= N) continue;
+    const float bn = bias[n];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m >= M) continue;
+        const float v = acc[i][j][r] + bn;
+        C[m * ldc + n] = silu_out ? silu_f(v) : v;
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64_t ldw, const float* bias, int64_t M,
@@ -538,6 +625,13 @@ hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64
 hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, int64_t M,
                            int64_t N, int64_t K, float* C, int64_t ldc, int silu_in, int silu_out, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % F_BK == 0 && lda % 4 == 0 && ldw % 4 == 0 && ((uintptr_t)A & 15) == 0 && ((uintptr_t)W & 15) == 0) {
+    const int tiles_n = (int)ceil_div(N, F_TILE);
+    const int64_t blocks = ceil_div(M, F_TILE) * tiles_n;
+    hipLaunchKernelGGL(k_gemm_f32m, dim3((unsigned)blocks), dim3(256), 0, s, A, lda, W, ldw, bias, M, N, K, C, ldc,
+                       silu_in, silu_out, tiles_n);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(M, 64));
   hipLaunchKernelGGL(k_gemm_f32, grid, dim3(256), 0, s, A, lda, W, ldw, bias, M, N, K, C, ldc, silu_in, silu_out);
   return hipGetLastError();

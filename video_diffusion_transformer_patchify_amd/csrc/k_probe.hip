@@ -26,12 +26,14 @@ __global__ __launch_bounds__(256, 1) void k_mfma_probe(float* sink, int64_t roun
   for (int i = tid; i < 32768; i += 256)
     lds[i] = random_operands ? (i < 16384 ? probe_val(i, 11u, 1.0f) : probe_val(i, 22u, 0.05f)) : (unsigned short)0;
   __syncthreads();
-  // the fragment layout of the large GEMM: 128-byte rows, chunk (2 ks + g) of row l32 of each 32-row block
+  // the fragment layout of the large GEMM: 128-byte rows whose 16-byte chunks are XOR-swizzled by the
+  // row (conflict-free reads of chunk 2 ks + g by 32 consecutive rows)
   const char* lx = (const char*)lds + (wave >> 1) * 16384;            // "activation" half
   const char* lw = (const char*)lds + 32768 + (wave & 1) * 16384;     // "weight" half
+  const int swz = ((l32 >> 1) ^ (l32 << 2)) & 7;
   int foff[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) foff[ks] = l32 * 128 + ((2 * ks + g) << 4);
+  for (int ks = 0; ks < 4; ++ks) foff[ks] = l32 * 128 + (((2 * ks + g) ^ swz) << 4);
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
