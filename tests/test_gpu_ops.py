@@ -94,8 +94,11 @@ def test_transpose_v_bitexact(G, B, L, nh, col_off, ld):
 # GEMM + epilogues
 # ------------------------------------------------------------------------------------------------
 
+# The last three reach the persistent 256x256 kernel (>= 512 tiles): ragged M (37 rows into a tile) and N
+# (8 columns into a tile) with a tile count that does not split evenly over the 8 XCDs; the minimum K of
+# 128 (four K stages, no steady-state iteration); and the full block shape.
 GEMM_CASES = [(1, 64, 64), (300, 192, 64), (4133, 1536, 1536), (452, 3072, 1536), (1000, 8960, 1536),
-              (777, 1536, 8960), (65520, 1536, 1536)]
+              (777, 1536, 8960), (4133, 8968, 1536), (9000, 4104, 128), (65520, 1536, 1536)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES)
