@@ -106,9 +106,32 @@ struct RmsArgs {
   int64_t rope_h_off, rope_w_off, rope_sin_off;  // float offsets of the h / w tables and of the sin half
 };
 
-template <int NV>
-__device__ __forceinline__ void rms_segment(const RmsArgs& a, bf16_t* p, const float* gamma, int lane, int64_t tok_f,
-                                            int64_t tok_h, int64_t tok_w) {
+// Rotation coefficients of one token for the 4 pairs a lane owns: in every 8-element chunk of every head
+// the lane holds channels 8 (lane % 16) .. +7 of the head, i.e. pairs m = 4 (lane % 16) .. +3, so the
+// same 4 (cos, sin) serve all heads and both segments of the row.
+struct RopeCoef {
+  float cs[4], sn[4];
+};
+
+__device__ __forceinline__ RopeCoef rope_coef(const RmsArgs& a, int lane, int64_t tok_f, int64_t tok_h, int64_t tok_w) {
+  RopeCoef rc;
+  const int m0 = 4 * (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = m0 + e;
+    int64_t off;
+    if (m < a.pt) off = tok_f * a.pt + m;
+    else if (m < a.pt + a.ph) off = a.rope_h_off + tok_h * a.ph + (m - a.pt);
+    else off = a.rope_w_off + tok_w * (64 - a.pt - a.ph) + (m - a.pt - a.ph);
+    rc.cs[e] = a.rope[off];
+    rc.sn[e] = a.rope[a.rope_sin_off + off];
+  }
+  return rc;
+}
+
+template <int NV, bool ROPE>
+__device__ __forceinline__ void rms_segment(const RmsArgs& a, bf16_t* p, const float* gamma, int lane,
+                                            const RopeCoef& rc) {
   u32x4 raw[NV];
   float s = 0.f;
 #pragma unroll
@@ -131,15 +154,9 @@ __device__ __forceinline__ void rms_segment(const RmsArgs& a, bf16_t* p, const f
     for (int e = 0; e < 4; ++e) {
       float x0 = lo_bf16(raw[i][e]) * rstd * gg[2 * e];
       float x1 = hi_bf16(raw[i][e]) * rstd * gg[2 * e + 1];
-      if (a.rope) {
-        const int m = ((c0 & 127) >> 1) + e;   // pair index inside the head
-        int64_t off;
-        if (m < a.pt) off = tok_f * a.pt + m;
-        else if (m < a.pt + a.ph) off = a.rope_h_off + tok_h * a.ph + (m - a.pt);
-        else off = a.rope_w_off + tok_w * (64 - a.pt - a.ph) + (m - a.pt - a.ph);
-        const float cs = a.rope[off], sn = a.rope[a.rope_sin_off + off];
-        const float r0 = x0 * cs - x1 * sn;
-        const float r1 = x0 * sn + x1 * cs;
+      if constexpr (ROPE) {
+        const float r0 = x0 * rc.cs[e] - x1 * rc.sn[e];
+        const float r1 = x0 * rc.sn[e] + x1 * rc.cs[e];
         x0 = r0; x1 = r1;
       }
       o[e] = pack_bf16x2(x0, x1);
@@ -161,8 +178,15 @@ __global__ __launch_bounds__(256) void k_rms_rope(RmsArgs a) {
     tf = n / ((int64_t)a.Wp * a.Hp);
   }
   bf16_t* r = a.buf + row * a.ld;
-  rms_segment<NV>(a, r + a.off_a, a.gamma_a, lane, tf, th, tw);
-  if (a.gamma_b) rms_segment<NV>(a, r + a.off_b, a.gamma_b, lane, tf, th, tw);
+  if (a.rope) {
+    const RopeCoef rc = rope_coef(a, lane, tf, th, tw);
+    rms_segment<NV, true>(a, r + a.off_a, a.gamma_a, lane, rc);
+    if (a.gamma_b) rms_segment<NV, true>(a, r + a.off_b, a.gamma_b, lane, rc);
+  } else {
+    const RopeCoef rc = {};
+    rms_segment<NV, false>(a, r + a.off_a, a.gamma_a, lane, rc);
+    if (a.gamma_b) rms_segment<NV, false>(a, r + a.off_b, a.gamma_b, lane, rc);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------------
