@@ -53,13 +53,21 @@ WAN_DEV float wave_max(float v) {
 }
 
 // GELU, tanh form.  0.5 u (1 + tanh z) equals u * sigmoid(2 z), z = sqrt(2/pi) (u + 0.044715 u^3).
+// GELU, tanh form: 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3), evaluated as u * sigmoid(2z)
+// = u / (1 + 2^(-2 z log2(e))) with the constants folded into one polynomial in u, v_exp_f32 and the
+// hardware reciprocal (about 1 ulp of fp32; a full IEEE division costs ~10 instructions).  Saturates
+// correctly: u -> -inf gives 2^(+inf) = inf and u * rcp(inf) = 0; u -> +inf gives u * rcp(1) = u.
 WAN_DEV float gelu_tanh_f(float u) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  float z = k0 * (u + 0.044715f * u * u * u);
-  return u / (1.0f + __expf(-2.0f * z));
+  constexpr float c1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  constexpr float c2 = c1 * 0.044715f;
+  const float e = __builtin_amdgcn_exp2f(u * fmaf(c2, u * u, c1));
+  return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-WAN_DEV float silu_f(float u) { return u / (1.0f + __expf(-u)); }
+// SiLU: u * sigmoid(u) = u / (1 + 2^(-u log2(e))), same evaluation as above.
+WAN_DEV float silu_f(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.4426950408889634f));
+}
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
