@@ -16,6 +16,8 @@ namespace {
 
 // ---------------------------------------------------------------------------------------------------
 // Residual add + LayerNorm + modulate / affine.  One wave per row; NV float4 per lane (D = 256 * NV).
+// The row streams (x in and out, the branch output, y) are touched once per launch and are far larger
+// than the caches, so they use non-temporal loads and stores; the small parameter vectors stay cached.
 // The residual step folds the previous branch into the fp32 stream before normalising it:
 //   res_mode 1: x += r            (cross-attention output, ungated)
 //   res_mode 2: x += r * gate,    gate = res_tab[d] + res_src[row(m)][d]   (gate_msa, c_gate_msa)
@@ -41,19 +43,19 @@ __global__ __launch_bounds__(256) void k_ln_mod(LnArgs a) {
   const int64_t sr = row / a.rows_per_src;
   f32x4 v[NV];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = *(const f32x4*)(xr + 4 * (lane + 64 * i));
+  for (int i = 0; i < NV; ++i) v[i] = __builtin_nontemporal_load((const f32x4*)(xr + 4 * (lane + 64 * i)));
   if (a.res_mode) {
     const bf16_t* rr = a.res + row * a.D;
     u32x2 rw[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) rw[i] = *(const u32x2*)(rr + 4 * (lane + 64 * i));
+    for (int i = 0; i < NV; ++i) rw[i] = __builtin_nontemporal_load((const u32x2*)(rr + 4 * (lane + 64 * i)));
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = 4 * (lane + 64 * i);
       f32x4 r = {lo_bf16(rw[i].x), hi_bf16(rw[i].x), lo_bf16(rw[i].y), hi_bf16(rw[i].y)};
       if (a.res_mode == 2) r *= *(const f32x4*)(a.res_tab + c) + *(const f32x4*)(a.res_src + sr * a.res_ld + c);
       v[i] += r;
-      *(f32x4*)(xr + c) = v[i];
+      __builtin_nontemporal_store(v[i], (f32x4*)(xr + c));
     }
   }
   float s = 0.f;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void k_ln_mod(LnArgs a) {
       f32x4 sh = *(const f32x4*)(a.tab_shift + c) + *(const f32x4*)(ssh + c);
       f32x4 o = (v[i] - mean) * rstd * (1.0f + sc) + sh;
       u32x2 w; w.x = pack_bf16x2(o.x, o.y); w.y = pack_bf16x2(o.z, o.w);
-      *(u32x2*)(yr + c) = w;
+      __builtin_nontemporal_store(w, (u32x2*)(yr + c));
     }
   } else {
 #pragma unroll
@@ -88,7 +90,93 @@ __global__ __launch_bounds__(256) void k_ln_mod(LnArgs a) {
       const int c = 4 * (lane + 64 * i);
       f32x4 o = (v[i] - mean) * rstd * *(const f32x4*)(a.gamma + c) + *(const f32x4*)(a.beta + c);
       u32x2 w; w.x = pack_bf16x2(o.x, o.y); w.y = pack_bf16x2(o.z, o.w);
-      *(u32x2*)(yr + c) = w;
+      __builtin_nontemporal_store(w, (u32x2*)(yr + c));
+    }
+  }
+}
+
+// Two rows per wave (narrow rows, D <= 1536): both rows' loads are in flight before either is reduced,
+// and the modulation / affine vectors are loaded once per sample and kept in registers.
+template <int NV>
+__device__ __forceinline__ void ln_load_params(const LnArgs& a, int64_t sr, int lane, f32x4 (&gt)[NV], f32x4 (&p0)[NV],
+                                               f32x4 (&p1)[NV]) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = 4 * (lane + 64 * i);
+    if (a.res_mode == 2) gt[i] = *(const f32x4*)(a.res_tab + c) + *(const f32x4*)(a.res_src + sr * a.res_ld + c);
+    if (a.mode == 0) {
+      p0[i] = 1.0f + (*(const f32x4*)(a.tab_scale + c) + *(const f32x4*)(a.src + sr * a.src_ld + a.src_scale_off + c));
+      p1[i] = *(const f32x4*)(a.tab_shift + c) + *(const f32x4*)(a.src + sr * a.src_ld + a.src_shift_off + c);
+    } else {
+      p0[i] = *(const f32x4*)(a.gamma + c);
+      p1[i] = *(const f32x4*)(a.beta + c);
+    }
+  }
+}
+
+template <int NV>
+__global__ __launch_bounds__(256) void k_ln_mod2(LnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+  if (row0 >= a.rows) return;
+  const int nr = row0 + 1 < a.rows ? 2 : 1;
+  f32x4 v[2][NV];
+  u32x2 rw[2][NV];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r < nr) {
+      const float* xr = a.x + (row0 + r) * a.D;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[r][i] = __builtin_nontemporal_load((const f32x4*)(xr + 4 * (lane + 64 * i)));
+      if (a.res_mode) {
+        const bf16_t* rr = a.res + (row0 + r) * a.D;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) rw[r][i] = __builtin_nontemporal_load((const u32x2*)(rr + 4 * (lane + 64 * i)));
+      }
+    }
+  }
+  int64_t sr_cached = -1;
+  f32x4 gt[NV], p0[NV], p1[NV];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (r >= nr) break;
+    const int64_t row = row0 + r;
+    const int64_t sr = row / a.rows_per_src;
+    if (sr != sr_cached) {
+      ln_load_params<NV>(a, sr, lane, gt, p0, p1);
+      sr_cached = sr;
+    }
+    float* xr = a.x + row * a.D;
+    if (a.res_mode) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = 4 * (lane + 64 * i);
+        f32x4 rv = {lo_bf16(rw[r][i].x), hi_bf16(rw[r][i].x), lo_bf16(rw[r][i].y), hi_bf16(rw[r][i].y)};
+        if (a.res_mode == 2) rv *= gt[i];
+        v[r][i] += rv;
+        __builtin_nontemporal_store(v[r][i], (f32x4*)(xr + c));
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) s += (v[r][i].x + v[r][i].y) + (v[r][i].z + v[r][i].w);
+    const float inv_d = 1.0f / (float)a.D;
+    const float mean = wave_sum(s) * inv_d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      f32x4 d = v[r][i] - mean;
+      q += (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + a.eps);
+    bf16_t* yr = a.y + row * a.D;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = 4 * (lane + 64 * i);
+      // mode 0: (x - mean) rstd (1 + scale) + shift; mode 1: (x - mean) rstd gamma + beta
+      f32x4 o = (v[r][i] - mean) * rstd * p0[i] + p1[i];
+      u32x2 w; w.x = pack_bf16x2(o.x, o.y); w.y = pack_bf16x2(o.z, o.w);
+      __builtin_nontemporal_store(w, (u32x2*)(yr + c));
     }
   }
 }
@@ -275,6 +363,18 @@ hipError_t launch_layernorm(float* x, int64_t rows, int64_t D, float eps, int mo
   if (D % 256 != 0 || D / 256 > 24) return hipErrorInvalidValue;
   LnArgs a{x, rows, D, eps, mode, tab_shift, tab_scale, src, src_ld, src_shift_off, src_scale_off,
            rows_per_src > 0 ? rows_per_src : 1, gamma, beta, res_mode, res, res_tab, res_src, res_ld, y};
+  if (D / 256 <= 6) {
+    dim3 grid((unsigned)ceil_div(rows, 8)), block(256);
+    switch (D / 256) {
+      case 1: hipLaunchKernelGGL(k_ln_mod2<1>, grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL(k_ln_mod2<2>, grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL(k_ln_mod2<3>, grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL(k_ln_mod2<4>, grid, block, 0, s, a); break;
+      case 5: hipLaunchKernelGGL(k_ln_mod2<5>, grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL(k_ln_mod2<6>, grid, block, 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)ceil_div(rows, 4)), block(256);
   switch (D / 256) {
 #define X(n) case n: hipLaunchKernelGGL(k_ln_mod<n>, grid, block, 0, s, a); break;
