@@ -217,20 +217,28 @@ __device__ __forceinline__ RopeCoef rope_coef(const RmsArgs& a, int lane, int64_
   return rc;
 }
 
-template <int NV, bool ROPE>
-__device__ __forceinline__ void rms_segment(const RmsArgs& a, bf16_t* p, const float* gamma, int lane,
-                                            const RopeCoef& rc) {
-  u32x4 raw[NV];
-  float s = 0.f;
+// NT: non-temporal loads (the q/k pass streams 400 MB+ once; a single segment written by the GEMM just
+// before is better served from the caches).
+template <int NV, bool NT>
+__device__ __forceinline__ void rms_load(const bf16_t* p, int lane, u32x4 (&raw)[NV]) {
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    raw[i] = *(const u32x4*)(p + 8 * (lane + 64 * i));
+    const u32x4* q = (const u32x4*)(p + 8 * (lane + 64 * i));
+    raw[i] = NT ? __builtin_nontemporal_load(q) : *q;
+  }
+}
+
+template <int NV, bool ROPE>
+__device__ __forceinline__ void rms_finish(const RmsArgs& a, bf16_t* p, const float* gamma, int lane, const RopeCoef& rc,
+                                           const u32x4 (&raw)[NV]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float lo = lo_bf16(raw[i][e]), hi = hi_bf16(raw[i][e]);
       s += lo * lo + hi * hi;
     }
-  }
   const float rstd = 1.0f / sqrtf(wave_sum(s) / (float)a.D + a.eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -253,7 +261,8 @@ __device__ __forceinline__ void rms_segment(const RmsArgs& a, bf16_t* p, const f
   }
 }
 
-template <int NV>
+// TWO: q and k segments in one row (the self-attention pass); otherwise one segment.
+template <int NV, bool TWO>
 __global__ __launch_bounds__(256) void k_rms_rope(RmsArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -266,14 +275,30 @@ __global__ __launch_bounds__(256) void k_rms_rope(RmsArgs a) {
     tf = n / ((int64_t)a.Wp * a.Hp);
   }
   bf16_t* r = a.buf + row * a.ld;
-  if (a.rope) {
-    const RopeCoef rc = rope_coef(a, lane, tf, th, tw);
-    rms_segment<NV, true>(a, r + a.off_a, a.gamma_a, lane, rc);
-    if (a.gamma_b) rms_segment<NV, true>(a, r + a.off_b, a.gamma_b, lane, rc);
+  if constexpr (TWO) {
+    // both segments' loads are in flight before either is reduced
+    u32x4 ra[NV], rb[NV];
+    rms_load<NV, true>(r + a.off_a, lane, ra);
+    rms_load<NV, true>(r + a.off_b, lane, rb);
+    if (a.rope) {
+      const RopeCoef rc = rope_coef(a, lane, tf, th, tw);
+      rms_finish<NV, true>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
+      rms_finish<NV, true>(a, r + a.off_b, a.gamma_b, lane, rc, rb);
+    } else {
+      const RopeCoef rc = {};
+      rms_finish<NV, false>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
+      rms_finish<NV, false>(a, r + a.off_b, a.gamma_b, lane, rc, rb);
+    }
   } else {
-    const RopeCoef rc = {};
-    rms_segment<NV, false>(a, r + a.off_a, a.gamma_a, lane, rc);
-    if (a.gamma_b) rms_segment<NV, false>(a, r + a.off_b, a.gamma_b, lane, rc);
+    u32x4 ra[NV];
+    rms_load<NV, false>(r + a.off_a, lane, ra);
+    if (a.rope) {
+      const RopeCoef rc = rope_coef(a, lane, tf, th, tw);
+      rms_finish<NV, true>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
+    } else {
+      const RopeCoef rc = {};
+      rms_finish<NV, false>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
+    }
   }
 }
 
@@ -399,7 +424,11 @@ hipError_t launch_rms_rope(bf16_t* buf, int64_t ld, int64_t rows, int64_t D, flo
   a.rope_sin_off = a.rope_w_off + (int64_t)Wp * (dw / 2);
   dim3 grid((unsigned)ceil_div(rows, 4)), block(256);
   switch (D / 512) {
-#define X(n) case n: hipLaunchKernelGGL(k_rms_rope<n>, grid, block, 0, s, a); break;
+#define X(n)                                                                 \
+  case n:                                                                    \
+    if (gamma_b) hipLaunchKernelGGL((k_rms_rope<n, true>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((k_rms_rope<n, false>), grid, block, 0, s, a);       \
+    break;
     NV_CASES(X)
 #undef X
     default: return hipErrorInvalidValue;
