@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmArgs a) {
 //    it; bf16 epilogues pass through LDS and leave as whole 256-byte row segments.
 // ---------------------------------------------------------------------------------------------------
 constexpr int BIG = 256;
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 2;
 constexpr int BK4 = 32;                          // K per stage
 constexpr int NSTAGE = 4;
 constexpr int OPND_BYTES = BIG * BK4 * 2;        // one operand tile, 16 KB
