@@ -360,7 +360,8 @@ def test_time_embed(G, rows, D, per_token):
 
 
 @pytest.mark.parametrize("rows,D,res_mode,per_token", [(300, 1536, 1, False), (1000, 3072, 2, False),
-                                                       (257, 5120, 2, True), (65520, 1536, 2, False)])
+                                                       (257, 5120, 2, True), (65520, 1536, 2, False),
+                                                       (301, 1536, 2, True), (77, 512, 1, False)])
 def test_layernorm_with_residual(G, rows, D, res_mode, per_token):
     """x += r (res_mode 1) or x += r * (tab + src[row]) (res_mode 2), then LN + modulation."""
     import torch
@@ -369,7 +370,8 @@ def test_layernorm_with_residual(G, rows, D, res_mode, per_token):
     xt = G.draw_normal(4, f"lrx{rows}{D}", (rows, D), "f32", 1.5)
     x = G.to_device(xt).clone()
     r, rh = G.bf16_dev((rows, D), f"lrr{rows}{D}", 0.7)
-    L = 1 if per_token else 100
+    # 99 rows per sample: sample boundaries fall inside the row pairs of the two-rows-per-wave kernel
+    L = 1 if per_token else 99
     nsrc = (rows + L - 1) // L
     tab_t = G.draw_normal(4, "lrtab", (6, D), "f32", 1.0 / math.sqrt(D))
     src_t = G.draw_normal(4, f"lrsrc{nsrc}{D}", (nsrc, 6 * D), "f32", 0.3)
