@@ -296,11 +296,18 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
 
   // One pipelined step: S(j+1) with P(j); PV(j) with max(S(j+1)).  LAST: S(j+1) is the final sub-tile.
   // Tile t+2 is requested during tile t (K in its first half, V in its second) into the buffer of tile
-  // t-1, which every wave finished reading before the barrier that ended tile t-1.  The barrier that
-  // ends tile t waits only for tile t+1.
+  // t-1.  The second half of tile t reads tile t+1 (the scores of its first sub-tile), so it starts with
+  // the workgroup barrier: own loads of tile t+1 landed (only the K loads of tile t+2 may be younger),
+  // every wave's loads of it landed, and every wave done with tile t-1, whose V part is refilled right
+  // after (its K part was last read in the second-to-last step before this barrier).
   auto step = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int t = j >> 1, half = j & 1;
+    if (half) {
+      if (t + 2 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0074);   // vmcnt(4) lgkmcnt(0)
+      else __builtin_amdgcn_s_waitcnt(0x0070);                   // vmcnt(0) lgkmcnt(0)
+      block_sync();
+    }
     if (t + 2 < n_tiles) issue(t + 2, half);
     u32x4 pf[2][2];
     scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
@@ -311,11 +318,6 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     pv(st, pf, lds[t % NBUF] + K_TILE_BYTES, half, l32, g);
     row_max(s_next, mx);
     maybe_rescale(st, mx, c, grow_thr);
-    if (half) {
-      if (t + 2 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) lgkmcnt(0): tile t+1 landed
-      else __builtin_amdgcn_s_waitcnt(0x0070);                   // vmcnt(0) lgkmcnt(0)
-      block_sync();
-    }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) s_cur[qb] = s_next[qb];
   };
