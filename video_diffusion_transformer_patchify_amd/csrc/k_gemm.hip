@@ -220,14 +220,10 @@ constexpr int SLOTS_PER_XCD = 32;                // CUs per XCD: one persistent 
 
 __device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// bf16 epilogue of one wave's 128 x 128 block through its LDS slice, 32 rows at a time.  Writes: lane
-// (l32, g) puts its 4 values of chunk c (= 8 output columns) of row l32 into 16-byte position
-// c ^ (l32 & 15), 8-byte half g ^ (l32 >> 4) (conflict-free); reads: 16 lanes per row take the row's
-// 16 chunks, so each store instruction writes 4 whole 256-byte row segments.
-template <int EPI>
-__device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[4][4], int64_t mb, int64_t nb,
-                                               char* slice, int lane, int l32, int g) {
-  f32x4 bias[4][4];
+// Bias values of the columns lane (l32, g) holds in a wave's 128 x 128 block starting at column nb:
+// bias[i][rg] covers columns nb + 32 i + 8 rg + 4 g .. + 3, which are accumulator elements 4 rg .. 4 rg + 3
+// of every acc[i][*].
+__device__ __forceinline__ void load_bias(const GemmArgs& a, int64_t nb, int g, f32x4 (&bias)[4][4]) {
   const bool full_n = nb + 128 <= a.N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -237,7 +233,21 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
       if (!full_n && n >= a.N) n = a.N - 4;
       bias[i][rg] = *(const f32x4*)(a.bias + n);
     }
+}
+
+// bf16 epilogue of one wave's 128 x 128 block (bias already in the accumulators) through its LDS slice,
+// 32 rows at a time.  Writes: lane (l32, g) puts its 4 values of chunk c (= 8 output columns) of row l32
+// into 16-byte position c ^ (l32 & 15), 8-byte half g ^ (l32 >> 4) (conflict-free); reads: 16 lanes per
+// row take the row's 16 chunks, so each store instruction writes 4 whole 256-byte row segments.  Blocks
+// wholly inside the output store without per-row checks, from a scalar row base and one 32-bit lane offset.
+template <int EPI>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (&acc)[4][4], int64_t mb, int64_t nb,
+                                               char* slice, int lane, int l32, int g) {
+  const bool full = mb + 128 <= a.M && nb + 128 <= a.N;
   const int wrow = l32 * 256 + 8 * (g ^ (l32 >> 4));
+  const int c16 = lane & 15, r4 = lane >> 4;
+  const uint32_t loff = (uint32_t)((r4 * a.ldo + 8 * c16) * 2);
+  char* const obase = (char*)a.out + (mb * a.ldo + nb) * 2;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
@@ -245,7 +255,6 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         f32x4 v = {acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
-        v += bias[i][rg];
         if constexpr (EPI == EPI_GELU_BF16) {
           v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
         }
@@ -259,11 +268,16 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const int row = 4 * s + (lane >> 4), c = lane & 15;
-      u32x4 d = *(const u32x4*)(slice + row * 256 + ((c ^ (row & 15)) << 4));
-      if (row >> 4) d = (u32x4){d.z, d.w, d.x, d.y};
-      const int64_t m = mb + 32 * j + row, n = nb + 8 * c;
-      if (m < a.M && (full_n || n < a.N)) *(u32x4*)((bf16_t*)a.out + m * a.ldo + n) = d;
+      const int row = 4 * s + r4;
+      u32x4 d = *(const u32x4*)(slice + row * 256 + ((c16 ^ (row & 15)) << 4));
+      if (s >= 4) d = (u32x4){d.z, d.w, d.x, d.y};   // rows 16..31 hold their halves swapped
+      char* const rowbase = obase + (int64_t)(32 * j + 4 * s) * a.ldo * 2;
+      if (full) {
+        *(u32x4*)(rowbase + loff) = d;
+      } else {
+        const int64_t m = mb + 32 * j + row, n = nb + 8 * c16;
+        if (m < a.M && n < a.N) *(u32x4*)(rowbase + loff) = d;
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): reads done before the next slab overwrites
     __builtin_amdgcn_wave_barrier();
@@ -273,7 +287,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES + 4 * EPI_SLICE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: read it into a scalar register so every LDS address of the direct
+  // loads (written to M0) is scalar arithmetic, with no per-load readfirstlane
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
 
@@ -317,8 +333,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   // instruction i of half h of stage kt: h = 0 the X tile, h = 1 the W tile
   auto dma = [&](int kt, int h, int i) {
     char* dst = lds + (kt % NSTAGE) * STAGE_BYTES + h * OPND_BYTES + (4 * wave + i) * 1024;
-    const char* src = (h ? wt + wo[i] : xt + xo[i]) + kt * BK4 * 2;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+    // scalar base + 32-bit lane offset: the load takes its address in saddr + voffset form
+    const char* base = (h ? wt : xt) + kt * BK4 * 2;
+    __builtin_amdgcn_global_load_lds((const void*)(base + (h ? wo[i] : xo[i])), (lds_void*)dst, 16, 0, 0);
   };
   // stages 0..2 whole and the first half of stage 3 (28 instructions)
   auto prologue = [&]() {
@@ -338,6 +355,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 
   f32x16 acc[4][4];
   u32x4 fa[2][4], fb[2][4];
+  // bf16 epilogues: the accumulators start from the bias, written by one MFMA each at tile start:
+  // A holds column n's bias split into bf16 hi + lo at k = 0, 1 (lane l32 of block i is column
+  // wn0 + 32 i + l32), B holds 1 at k = 0, 1, so D[n][m] = hi + lo = bias[n] to ~2^-18 relative.
+  constexpr bool FOLD = EPI == EPI_BF16 || EPI == EPI_GELU_BF16;
+  float bcol[4];
+  auto bias_cols = [&](int64_t nb, int i) {   // bias of column nb + 32 i + l32 (clamped past N)
+    const int64_t n = nb + 32 * i + l32;
+    return a.bias[n < a.N ? n : a.N - 1];
+  };
   // fragment q (0..7) of k-substep ks of stage kt: q < 4 -> W rows wn0 + 32 q, else X rows
   auto frag = [&](int kt, int ks, int q) {
     const char* base = lds + (kt % NSTAGE) * STAGE_BYTES;
@@ -357,19 +383,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   //   B: MFMAs of substep 1 | substep-0 fragments of stage kt+1 | first half of stage kt+4, which goes
   //      into stage kt's buffer (free once every wave has passed the barrier)
   // WAIT = stages allowed in flight at the barrier (8 instructions each).
-  auto step = [&](int kt, auto issue_a, auto issue_b, auto wait_n, auto next) {
+  //   BIAS (third-last step): the 4 bias loads of the next tile go out in phase A, after every direct
+  //   load of this tile, so the barrier allows them in flight too (WAIT = 3: vmcnt(12)).
+  int64_t bias_nb = 0;   // first column of this wave's block in the next tile
+  auto step = [&](int kt, auto issue_a, auto issue_b, auto wait_n, auto next, auto bias_next) {
     constexpr bool IA = decltype(issue_a)::value, IB = decltype(issue_b)::value;
-    constexpr bool NEXT = decltype(next)::value;
+    constexpr bool NEXT = decltype(next)::value, BIAS = decltype(bias_next)::value;
     constexpr int WAIT = decltype(wait_n)::value;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       mma(0, q);
       frag(kt, 1, q);
       if (IA && (q & 1)) dma(kt + 3, 1, q >> 1);
+      if (BIAS && q < 4) bcol[q] = bias_cols(bias_nb, q);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (NEXT) {
-      if constexpr (WAIT == 2) __builtin_amdgcn_s_waitcnt(0x4070);        // vmcnt(16) lgkmcnt(0)
+      if constexpr (WAIT == 3) __builtin_amdgcn_s_waitcnt(0x007C);        // vmcnt(12) lgkmcnt(0)
+      else if constexpr (WAIT == 2) __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt(16) lgkmcnt(0)
       else if constexpr (WAIT == 1) __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8) lgkmcnt(0)
       else __builtin_amdgcn_s_waitcnt(0x0070);                            // vmcnt(0) lgkmcnt(0)
       block_sync();
@@ -385,6 +416,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   };
   using T = std::true_type;
   using F = std::false_type;
+  using W3 = std::integral_constant<int, 3>;
   using W2 = std::integral_constant<int, 2>;
   using W1 = std::integral_constant<int, 1>;
   using W0 = std::integral_constant<int, 0>;
@@ -392,12 +424,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   char* slice = lds + NSTAGE * STAGE_BYTES + wave * EPI_SLICE;
 
   setup(t);
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bcol[i] = bias_cols(n0 + wn0, i);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), once per workgroup, before any direct load
+  }
   prologue();
   while (true) {
+    if constexpr (FOLD) {
+      const u32x4 ones = {g ? 0u : 0x3F803F80u, 0u, 0u, 0u};   // bf16 1.0 at k = 0, 1
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const float hi = lo_bf16(pack_bf16x2(bcol[i], 0.f));           // bias rounded to bf16
+        const u32x4 bf = {g ? 0u : pack_bf16x2(bcol[i], bcol[i] - hi), 0u, 0u, 0u};   // hi, then the rest
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(bf), as_bf16x8(ones), (f32x16){}, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    }
     // stage 0 landed.  Outstanding: this tile's 28 direct loads, and possibly the previous tile's
     // epilogue stores (or loads issued after the 28).  Loads complete in order, so once at most 20
     // operations remain, the first 8 loads (stage 0) are done whatever the stores did.
@@ -405,15 +454,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     block_sync();
 #pragma unroll
     for (int q = 0; q < 8; ++q) frag(0, 0, q);
-    int kt = 0;
-    for (; kt + 4 < nk; ++kt) step(kt, T{}, T{}, W2{}, T{});
-    step(kt, T{}, F{}, W2{}, T{});
-    step(kt + 1, F{}, F{}, W1{}, T{});
-    step(kt + 2, F{}, F{}, W0{}, T{});
-    step(kt + 3, F{}, F{}, W0{}, F{});
-    const int64_t tm0 = m0, tn0 = n0;
     const int tnext = t + SLOTS_PER_XCD;
     const bool more = tnext < hi;
+    if constexpr (FOLD) {
+      // the next tile's columns (after the last tile: this tile's again, loaded and never used)
+      const int tt = more ? tnext : t;
+      const int width = GROUP_M * a.tiles_n;
+      const int first_m = (tt / width) * GROUP_M;
+      const int gsz = min(a.tiles_m - first_m, GROUP_M);
+      bias_nb = (int64_t)((tt % width) / gsz) * BIG + wn0;
+    }
+    int kt = 0;
+    for (; kt + 4 < nk; ++kt) step(kt, T{}, T{}, W2{}, T{}, F{});
+    step(kt, T{}, F{}, W2{}, T{}, F{});
+    if constexpr (FOLD) step(kt + 1, F{}, F{}, W3{}, T{}, T{});
+    else step(kt + 1, F{}, F{}, W1{}, T{}, F{});
+    step(kt + 2, F{}, F{}, W0{}, T{}, F{});
+    step(kt + 3, F{}, F{}, W0{}, F{}, F{});
+    const int64_t tm0 = m0, tn0 = n0;
     // every wave has read its last fragments before any wave refills the stages
     block_sync();
     if (more) {
