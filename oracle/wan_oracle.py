@@ -343,12 +343,14 @@ def head_forward(x: np.ndarray, temb: np.ndarray, w: dict, eps: float = 1e-6) ->
 
 
 def forward(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, workers: int = 1,
-            return_stages: bool = False, drop=None):
+            return_stages: bool = False, drop=None, checkpoint=None):
     """latent [B,C_in,F,H_z,W_z], t [B] or [B,L], text [B,Lt,4096] -> velocity [B,C_out,F,H_z,W_z].
 
     cfg carries the geometry (dim, num_heads, num_layers, eps, rope split/theta, freq_dim, out_channels).
     weights: dict name -> array, or an object with .f64(name).  drop(prefix) is called after each block
-    so lazily generated weights can be released.
+    so lazily generated weights can be released.  checkpoint, if given, has load() -> (next_block, x) or
+    None and save(next_block, x): a long run resumes from the token stream saved after its last finished
+    block (it changes no arithmetic).
     """
     w = weights
     latent = np.asarray(latent, dtype=np.float64)
@@ -359,8 +361,15 @@ def forward(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, w
     ctx = text_embed(np.asarray(text, dtype=np.float64), w)
     ang = rope_angles(fp, hp, wp, cfg.head_dim, cfg.rope_dims, cfg.rope_theta)
     stages = {"x0": x, "temb": temb, "tproj": tproj, "ctx": ctx, "ang": ang}
-    for kb in range(cfg.num_layers):
+    start = 0
+    if checkpoint is not None:
+        saved = checkpoint.load()
+        if saved is not None:
+            start, x = saved
+    for kb in range(start, cfg.num_layers):
         x = block_forward(x, ctx, tproj, ang, w, f"blocks.{kb}.", cfg.num_heads, cfg.eps, workers)
+        if checkpoint is not None and kb + 1 < cfg.num_layers:
+            checkpoint.save(kb + 1, x)
         if drop is not None:
             drop(f"blocks.{kb}.")
     z = head_forward(x, temb, w, cfg.eps)

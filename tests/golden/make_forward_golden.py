@@ -6,6 +6,10 @@ generator on both sides, so only the oracle's outputs are stored.  This script c
 and the seeded generator.
 
 usage: python tests/golden/make_forward_golden.py CFG_ID [--layers N] [--samples S] [--workers W]
+                                                      [--checkpoint DIR]
+
+With --checkpoint, the token stream after each finished block is kept in DIR (one file per workload and
+depth, tagged with the oracle's source hash) and an interrupted run resumes from it.
 """
 from __future__ import annotations
 
@@ -34,12 +38,40 @@ def golden_path(cfg_id: int, layers: int) -> str:
     return os.path.join(HERE, f"forward_cfg{cfg_id}_L{layers}.npz")
 
 
+class BlockCheckpoint:
+    """Keeps the oracle's token stream after the last finished block in one .npy file (+ a small header)."""
+
+    def __init__(self, directory: str, cfg_id: int, layers: int):
+        os.makedirs(directory, exist_ok=True)
+        stem = os.path.join(directory, f"forward_cfg{cfg_id}_L{layers}")
+        self.data, self.head = stem + ".x.npy", stem + ".head.npz"
+        self.tag = oracle_hash()
+
+    def load(self):
+        if not (os.path.exists(self.data) and os.path.exists(self.head)):
+            return None
+        h = np.load(self.head)
+        if str(h["oracle"][0]) != self.tag:
+            print("  checkpoint written by another oracle version: starting over", flush=True)
+            return None
+        nb = int(h["next_block"][0])
+        print(f"  resuming at block {nb}", flush=True)
+        return nb, np.load(self.data)
+
+    def save(self, next_block: int, x: np.ndarray):
+        np.save(self.data + ".tmp.npy", x)
+        os.replace(self.data + ".tmp.npy", self.data)
+        np.savez(self.head + ".tmp.npz", next_block=np.array([next_block]), oracle=np.array([self.tag]))
+        os.replace(self.head + ".tmp.npz", self.head)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("cfg_id", type=int)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--samples", type=int, default=32768)
     ap.add_argument("--workers", type=int, default=8)
+    ap.add_argument("--checkpoint", default=None, help="directory for per-block resume state")
     args = ap.parse_args()
     cfg = get_config(args.cfg_id)
     if args.layers is not None:
@@ -52,7 +84,8 @@ def main():
         w.drop(prefix)
         print(f"  {prefix} done at {time.time() - t0:.0f}s", flush=True)
 
-    out = O.forward(cfg, w, lat.f64(), t.f64(), txt.f64(), workers=args.workers, drop=drop)
+    ck = BlockCheckpoint(args.checkpoint, args.cfg_id, cfg.num_layers) if args.checkpoint else None
+    out = O.forward(cfg, w, lat.f64(), t.f64(), txt.f64(), workers=args.workers, drop=drop, checkpoint=ck)
     elapsed = time.time() - t0
     rng = np.random.default_rng(12345)
     n = out.size
