@@ -173,6 +173,60 @@ def probe(cfg):
     print("probe done", flush=True)
 
 
+def vendor_reference(cfg):
+    """Context, not part of the headline: the vendor libraries on the workload's shapes, same process.
+    Each GEMM of the block runs through this library and through hipBLASLt (torch.matmul, bf16 out)
+    on identical inputs; self-attention through this library and through torch's SDPA."""
+    import torch
+
+    from video_diffusion_transformer_patchify_amd import binding as Bd
+
+    def timed(f, reps):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    torch.cuda.set_device(0)
+    B, L, D, nh, Fd = cfg.batch, cfg.tokens, cfg.dim, cfg.num_heads, cfg.ffn_dim
+    M = B * L
+    g = torch.Generator(device="cuda").manual_seed(0)
+    res = {"gemm": [], "attention": {}}
+    for name, N, K in (("qkv", 3 * D, D), ("o", D, D), ("ffn1", Fd, D), ("ffn2", D, Fd)):
+        x = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+        w = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        wt = w.t()
+        b = torch.zeros(N, device="cuda")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ours = timed(lambda: Bd.op_gemm(x, w, b, Bd.EPI_BF16, out), 10)
+        blas = timed(lambda: torch.matmul(x, wt, out=out), 10)
+        fl = 2.0 * M * N * K
+        res["gemm"].append({"name": name, "M": M, "N": N, "K": K, "ours_ms": round(ours, 4),
+                            "hipblaslt_ms": round(blas, 4), "ours_tflops": round(fl / ours / 1e9, 1),
+                            "hipblaslt_tflops": round(fl / blas / 1e9, 1)})
+        del x, w, wt, out
+    fl = 4.0 * B * L * L * D
+    qkv = torch.randn((M, 3 * D), generator=g, device="cuda").to(torch.bfloat16)
+    ldv = (L + 63) // 64 * 64
+    vt = Bd.op_transpose_v(qkv, 2 * D, B, L, nh, ldv)
+    o = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
+    ours = timed(lambda: Bd.op_attention(qkv, qkv[:, D:], vt, o, B, L, L, nh), 5)
+    res["attention"]["ours_ms"] = round(ours, 3)
+    res["attention"]["ours_tflops"] = round(fl / ours / 1e9, 1)
+    del qkv, vt, o
+    q, k, v = (torch.randn((B, nh, L, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    sdpa = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v), 3)
+    res["attention"]["torch_sdpa_ms"] = round(sdpa, 3)
+    res["attention"]["torch_sdpa_tflops"] = round(fl / sdpa / 1e9, 1)
+    print(json.dumps({"vendor_reference": res, "workload": cfg.name}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,14 +236,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--probe", action="store_true", help="run the counter-calibration kernels only (for rocprofv3 --pmc)")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="time hipBLASLt GEMMs and torch SDPA next to this library's kernels on the workload's shapes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
-    if args.probe:
+    if args.probe or args.vendor_reference:
         from wan_inputs import get_config
 
-        probe(get_config(args.config))
+        (probe if args.probe else vendor_reference)(get_config(args.config))
         return
 
     import numpy as np  # noqa: F401
