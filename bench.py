@@ -302,6 +302,21 @@ def main():
     model.close()
     del latent, text, out
     torch.cuda.empty_cache()
+    # measured HBM bandwidth on this device: a plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB)
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    print(f"# HBM copy: {copy_gbps:.0f} GB/s (read + write)", file=sys.stderr, flush=True)
+    del src, dst
+    torch.cuda.empty_cache()
 
     res = {
         "metric": "DiT fwd ms/step + MFMA TFLOP/s, Wan-1.3B geometry, 32760 tokens bf16",
@@ -326,6 +341,8 @@ def main():
         "mfma_peak_measured": {"zero_operands": round(peak_zero, 1), "random_operands": round(peak_rand, 1),
                                "unit": "TFLOP/s", "kernel": "wan_probe_mfma (GEMM inner loop from LDS, 32x32x16 bf16)"},
         "mfma_frac_of_measured_random": round(tflops / peak_rand, 4),
+        "hbm_peak_measured": {"copy": round(copy_gbps, 1), "unit": "GB/s", "vendor": 8000.0,
+                              "kernel": "torch copy_ of 1 GiB (reads 1 GiB, writes 1 GiB)"},
         "flops_per_step": fl["total"],
         "roofline": {"kernel": "k_flash_attn<self> (self-attention)", "bound": "mfma", "achieved": round(attn_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tf / PEAK_BF16_TFLOPS, 4),
