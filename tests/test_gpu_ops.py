@@ -304,13 +304,15 @@ def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None):
         assert G.max_abs(g, ref) < 2e-2 * max(1.0, np.abs(ref).max())
 
 
-@pytest.mark.parametrize("B,L,nh", [(1, 320, 12), (2, 1000, 3), (1, 64, 2), (1, 1, 1), (2, 129, 4), (1, 7920, 2)])
+@pytest.mark.parametrize("B,L,nh", [(1, 320, 12), (2, 1000, 3), (1, 64, 2), (1, 1, 1), (1, 100, 2), (2, 129, 4),
+                                    (1, 7920, 2)])
 def test_self_attention(G, B, L, nh):
     G.note(f"self attention B={B} L={L} nh={nh}")
     _attn_case(G, B, L, L, nh, True, f"sa{B}_{L}_{nh}")
 
 
-@pytest.mark.parametrize("B,Lq,Lkv,nh", [(2, 320, 226, 12), (1, 1000, 512, 4), (2, 77, 1, 2), (1, 200, 64, 3)])
+@pytest.mark.parametrize("B,Lq,Lkv,nh", [(2, 320, 226, 12), (1, 1000, 512, 4), (2, 77, 1, 2), (1, 200, 64, 3),
+                                          (1, 150, 70, 2)])
 def test_cross_attention(G, B, Lq, Lkv, nh):
     G.note(f"cross attention B={B} Lq={Lq} Lkv={Lkv} nh={nh}")
     _attn_case(G, B, Lq, Lkv, nh, False, f"ca{B}_{Lq}_{Lkv}_{nh}")
