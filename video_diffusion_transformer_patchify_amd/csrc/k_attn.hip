@@ -11,8 +11,9 @@
 //     MFMA of one block per wave).  Q stays in registers.
 //   * K [key][d] and the pre-transposed V (Vt[b][h][d][key], so a tile is [d][key]) are copied
 //     global -> LDS in tiles of 64 keys with gfx950's direct loads (global_load_lds_dwordx4: lane l of
-//     an instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), no register staging, three
-//     buffers: while tile t is consumed, tile t+1 is resident and tile t+2 is in flight.  The 16-byte
+//     an instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), no register staging, four
+//     buffers: the one barrier per tile (in its second half) is followed by the K copies of tile t+4
+//     and the V copies of tile t+3, so each load has four to six 32-key steps to land.  The 16-byte
 //     chunks of each LDS row are XOR-swizzled so the fragment reads are free of bank conflicts; the
 //     swizzle is applied by choosing which global chunk each lane fetches.
 //   * Scores are formed transposed, S^T = K Q^T: the accumulator's column is the lane's query, so the
@@ -38,7 +39,7 @@ namespace {
 
 constexpr int KT = 64;              // keys per LDS tile
 constexpr int KS = 32;              // keys per sub-tile
-constexpr int NBUF = 3;             // LDS tile buffers
+constexpr int NBUF = 4;             // LDS tile buffers
 constexpr int QWAVE = 64;           // queries per wave (two 32-query blocks)
 constexpr int QB = 4 * QWAVE;       // queries per workgroup
 constexpr int K_TILE_BYTES = KT * 256;     // 64 rows of 128 bf16
@@ -276,16 +277,25 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   const float grow_thr = RESCALE_LOG2 / c;   // raw-score margin before the max is raised
   const int last_lim = (int)(a.Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
 
-  // ---- prologue: tiles 0 and 1 requested, tile 0 resident; scores and max of sub-tile 0
+  // vmcnt(n) for n in {0, 4, 8, 12, 16}, with or without lgkmcnt(0)
+  auto wait_vm = [&](int n, auto lgkm0) {
+    constexpr bool L0 = decltype(lgkm0)::value;
+    if (n >= 16) __builtin_amdgcn_s_waitcnt(L0 ? 0x4070 : 0x4F70);
+    else if (n >= 12) __builtin_amdgcn_s_waitcnt(L0 ? 0x007C : 0x0F7C);
+    else if (n >= 8) __builtin_amdgcn_s_waitcnt(L0 ? 0x0078 : 0x0F78);
+    else if (n >= 4) __builtin_amdgcn_s_waitcnt(L0 ? 0x0074 : 0x0F74);
+    else __builtin_amdgcn_s_waitcnt(L0 ? 0x0070 : 0x0F70);
+  };
+  // ---- prologue: K0, then [K1 V0] [K2 V1] [K3 V2] (the batches the barriers of tiles -3..-1 would
+  //      issue); tile 0 resident; scores and max of sub-tile 0
   issue(0, 0);
-  issue(0, 1);
-  if (n_tiles > 1) {
-    issue(1, 0);
-    issue(1, 1);
-    __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): own part of tile 0 landed (loads complete in order)
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#pragma unroll
+  for (int b = 1; b <= 3; ++b) {
+    if (b < n_tiles) issue(b, 0);
+    if (b - 1 < n_tiles) issue(b - 1, 1);
   }
+  // own loads younger than V0: [K2 V1] [K3 V2]
+  wait_vm(4 * ((2 < n_tiles) + (1 < n_tiles) + (3 < n_tiles) + (2 < n_tiles)), std::false_type{});
   block_sync();
   f32x16 s_cur[2], s_next[2];
   float mx[2];
@@ -295,20 +305,23 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   maybe_rescale(st, mx, c, grow_thr);
 
   // One pipelined step: S(j+1) with P(j); PV(j) with max(S(j+1)).  LAST: S(j+1) is the final sub-tile.
-  // Tile t+2 is requested during tile t (K in its first half, V in its second) into the buffer of tile
-  // t-1.  The second half of tile t reads tile t+1 (the scores of its first sub-tile), so it starts with
-  // the workgroup barrier: own loads of tile t+1 landed (only the K loads of tile t+2 may be younger),
-  // every wave's loads of it landed, and every wave done with tile t-1, whose V part is refilled right
-  // after (its K part was last read in the second-to-last step before this barrier).
+  // The second half of tile t reads tile t+1 (the scores of its first sub-tile), so it opens with the
+  // workgroup barrier: own loads of tile t+1 landed, then every wave's; every wave is also past its
+  // last read of K(t) (first half of tile t) and of V(t-1) (second half of tile t-1), whose LDS
+  // regions take K(t+4) and V(t+3) right after.
   auto step = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int t = j >> 1, half = j & 1;
     if (half) {
-      if (t + 2 < n_tiles) __builtin_amdgcn_s_waitcnt(0x0074);   // vmcnt(4) lgkmcnt(0)
-      else __builtin_amdgcn_s_waitcnt(0x0070);                   // vmcnt(0) lgkmcnt(0)
+      // tile t+1 landed: its V went out in the batch two barriers back; younger is the batch one back,
+      // [K(t+3) V(t+2)]
+      wait_vm(4 * ((t + 3 < n_tiles) + (t + 2 < n_tiles)), std::true_type{});
       block_sync();
+      // K part of tile t's buffer (last read: the scores in the first half) and V part of tile t-1's
+      // buffer (last read: the second half of tile t-1) are free
+      if (t + 4 < n_tiles) issue(t + 4, 0);
+      if (t + 3 < n_tiles) issue(t + 3, 1);
     }
-    if (t + 2 < n_tiles) issue(t + 2, half);
     u32x4 pf[2][2];
     scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
     probs(st, s_cur, pf, c);
