@@ -11,9 +11,10 @@
 //     MFMA of one block per wave).  Q stays in registers.
 //   * K [key][d] and the pre-transposed V (Vt[b][h][d][key], so a tile is [d][key]) are copied
 //     global -> LDS in tiles of 64 keys with gfx950's direct loads (global_load_lds_dwordx4: lane l of
-//     an instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), no register staging, four
-//     buffers: the one barrier per tile (in its second half) is followed by the K copies of tile t+4
-//     and the V copies of tile t+3, so each load has four to six 32-key steps to land.  The 16-byte
+//     an instruction fills bytes 16 l .. 16 l + 15 of a 1 KB LDS block), no register staging, five
+//     buffers (160 KB): one workgroup barrier per two tiles, each followed by the K copies of tiles
+//     t+4, t+5 and the V copies of tiles t+3, t+4, so every load has at least four 32-key steps to
+//     land.  The 16-byte
 //     chunks of each LDS row are XOR-swizzled so the fragment reads are free of bank conflicts; the
 //     swizzle is applied by choosing which global chunk each lane fetches.
 //   * Scores are formed transposed, S^T = K Q^T: the accumulator's column is the lane's query, so the
@@ -39,7 +40,7 @@ namespace {
 
 constexpr int KT = 64;              // keys per LDS tile
 constexpr int KS = 32;              // keys per sub-tile
-constexpr int NBUF = 4;             // LDS tile buffers
+constexpr int NBUF = 5;             // LDS tile buffers
 constexpr int QWAVE = 64;           // queries per wave (two 32-query blocks)
 constexpr int QB = 4 * QWAVE;       // queries per workgroup
 constexpr int K_TILE_BYTES = KT * 256;     // 64 rows of 128 bf16
@@ -288,14 +289,18 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   };
   // ---- prologue: K0, then [K1 V0] [K2 V1] [K3 V2] (the batches the barriers of tiles -3..-1 would
   //      issue); tile 0 resident; scores and max of sub-tile 0
+  // batches of the barriers of tiles -4 and -2: [K0 K1 V0] [K2 K3 V1 V2]
   issue(0, 0);
+  if (1 < n_tiles) issue(1, 0);
+  issue(0, 1);
 #pragma unroll
-  for (int b = 1; b <= 3; ++b) {
+  for (int b = 2; b <= 3; ++b)
     if (b < n_tiles) issue(b, 0);
-    if (b - 1 < n_tiles) issue(b - 1, 1);
-  }
-  // own loads younger than V0: [K2 V1] [K3 V2]
-  wait_vm(4 * ((2 < n_tiles) + (1 < n_tiles) + (3 < n_tiles) + (2 < n_tiles)), std::false_type{});
+#pragma unroll
+  for (int b = 1; b <= 2; ++b)
+    if (b < n_tiles) issue(b, 1);
+  // own loads younger than V0: K2 K3 V1 V2
+  wait_vm(4 * ((2 < n_tiles) + (3 < n_tiles) + (1 < n_tiles) + (2 < n_tiles)), std::false_type{});
   block_sync();
   f32x16 s_cur[2], s_next[2];
   float mx[2];
@@ -305,22 +310,23 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   maybe_rescale(st, mx, c, grow_thr);
 
   // One pipelined step: S(j+1) with P(j); PV(j) with max(S(j+1)).  LAST: S(j+1) is the final sub-tile.
-  // The second half of tile t reads tile t+1 (the scores of its first sub-tile), so it opens with the
-  // workgroup barrier: own loads of tile t+1 landed, then every wave's; every wave is also past its
-  // last read of K(t) (first half of tile t) and of V(t-1) (second half of tile t-1), whose LDS
-  // regions take K(t+4) and V(t+3) right after.
+  // The second half of an even tile t opens with the workgroup barrier that covers the next four
+  // steps, which read tiles t, t+1 and t+2 only: own loads of tiles t+1 and t+2 landed (both went out
+  // at the previous barrier or in the prologue: vmcnt(0)), then every wave's.  Every wave is also past
+  // its last read of K(t) (first half of tile t) and of V(t-1) (second half of tile t-1), so the K
+  // regions of tiles <= t and the V regions of tiles <= t-1 take K(t+4), K(t+5), V(t+3), V(t+4).
   auto step = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int t = j >> 1, half = j & 1;
-    if (half) {
-      // tile t+1 landed: its V went out in the batch two barriers back; younger is the batch one back,
-      // [K(t+3) V(t+2)]
-      wait_vm(4 * ((t + 3 < n_tiles) + (t + 2 < n_tiles)), std::true_type{});
+    if (half && !(t & 1)) {
+      // tiles t+1 and t+2 landed (all issued at the previous barrier or before), then every wave's
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
       block_sync();
-      // K part of tile t's buffer (last read: the scores in the first half) and V part of tile t-1's
-      // buffer (last read: the second half of tile t-1) are free
+      // free: K regions of tiles <= t, V regions of tiles <= t-1
       if (t + 4 < n_tiles) issue(t + 4, 0);
+      if (t + 5 < n_tiles) issue(t + 5, 0);
       if (t + 3 < n_tiles) issue(t + 3, 1);
+      if (t + 4 < n_tiles) issue(t + 4, 1);
     }
     u32x4 pf[2][2];
     scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
