@@ -220,21 +220,6 @@ constexpr int SLOTS_PER_XCD = 32;                // CUs per XCD: one persistent 
 
 __device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-// Bias values of the columns lane (l32, g) holds in a wave's 128 x 128 block starting at column nb:
-// bias[i][rg] covers columns nb + 32 i + 8 rg + 4 g .. + 3, which are accumulator elements 4 rg .. 4 rg + 3
-// of every acc[i][*].
-__device__ __forceinline__ void load_bias(const GemmArgs& a, int64_t nb, int g, f32x4 (&bias)[4][4]) {
-  const bool full_n = nb + 128 <= a.N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      int64_t n = nb + 32 * i + 8 * rg + 4 * g;
-      if (!full_n && n >= a.N) n = a.N - 4;
-      bias[i][rg] = *(const f32x4*)(a.bias + n);
-    }
-}
-
 // bf16 epilogue of one wave's 128 x 128 block (bias already in the accumulators) through its LDS slice,
 // 32 rows at a time.  Writes: lane (l32, g) puts its 4 values of chunk c (= 8 output columns) of row l32
 // into 16-byte position c ^ (l32 & 15), 8-byte half g ^ (l32 >> 4) (conflict-free); reads: 16 lanes per
