@@ -67,7 +67,8 @@ def traffic_for(kernel_file: str):
 
 
 def time_self_attention(B, cfg, reps, stream):
-    """Average duration of the self-attention kernel at the workload's shape, HIP events on its stream."""
+    """Average duration of the self-attention kernel at the workload's shape, HIP events on its stream; launched
+    as the forward launches it (with its workspace, so a short last round of workgroups is key-split)."""
     import torch
 
     from video_diffusion_transformer_patchify_amd import binding as Bd
@@ -78,16 +79,17 @@ def time_self_attention(B, cfg, reps, stream):
     ldv = (L + 63) // 64 * 64
     vt = Bd.op_transpose_v(qkv, 2 * D, B, L, nh, ldv, stream=stream)
     out = torch.empty((B * L, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(Bd.attention_workspace_bytes() // 4, dtype=torch.float32, device="cuda")
     for _ in range(2):
-        Bd.op_attention(qkv, qkv[:, D:], vt, out, B, L, L, nh, stream=stream)
+        Bd.op_attention_ws(qkv, qkv[:, D:], vt, out, B, L, L, nh, workspace=ws, stream=stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
     for _ in range(reps):
-        Bd.op_attention(qkv, qkv[:, D:], vt, out, B, L, L, nh, stream=stream)
+        Bd.op_attention_ws(qkv, qkv[:, D:], vt, out, B, L, L, nh, workspace=ws, stream=stream)
     ev1.record(stream)
     ev1.synchronize()
     ms = ev0.elapsed_time(ev1) / reps
-    del qkv, vt, out
+    del qkv, vt, out, ws
     return ms
 
 

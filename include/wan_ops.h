@@ -95,6 +95,19 @@ wan_status wan_op_transpose_v(const void* src, int64_t ld, int64_t col_off, int6
 wan_status wan_op_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt, int64_t ldv,
                             void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh, void* stream);
 
+/* The same attention with a caller-owned device workspace of wan_op_attention_workspace_bytes() bytes
+ * (fp32-aligned; contents need no initialisation).  Workgroups are (batch, head, 256-query tile) units,
+ * one per CU at a time; when the last round of units would occupy at most half of the CUs, its units are
+ * split into key chunks of a multiple of 64 keys, each chunk writes its unnormalised output, row max
+ * and row sum to the workspace, and a merge pass forms the softmax over all keys from them
+ * (o = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c).  Results equal wan_op_attention's up to fp32
+ * rounding.  The workspace is in use until the call's work on `stream` completes; calls that overlap
+ * on one workspace race.  Errors: WAN_ERR_INVALID_ARG for a NULL or short workspace. */
+wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt, int64_t ldv,
+                               void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh, void* workspace,
+                               int64_t workspace_bytes, void* stream);
+int64_t wan_op_attention_workspace_bytes(void);
+
 /* Timestep embedding, fp32 throughout (WanAnimate page, configuration section: freq_dim 256, the
  * time embedder kept in fp32; WanPipeline notes: temb (B, D), timestep_proj (B, 6D)):
  *   s = [cos(t w_i), sin(t w_i)], w_i = 10000^(-i/(freq_dim/2))

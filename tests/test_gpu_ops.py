@@ -271,7 +271,7 @@ def test_rms_norm_single_segment(G):
 # ------------------------------------------------------------------------------------------------
 
 
-def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None):
+def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None, split=False):
     import torch
 
     D = 128 * nh
@@ -290,7 +290,10 @@ def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None):
         kh, vh = kvh[:, :D], kvh[:, D:]
         vt = G.B.op_transpose_v(kv, D, B, Lkv, nh, _round_up(Lkv, 64))
     out = torch.empty((B * Lq, D), dtype=torch.bfloat16, device="cuda")
-    G.B.op_attention(q, k, vt, out, B, Lq, Lkv, nh)
+    if split:
+        G.B.op_attention_ws(q, k, vt, out, B, Lq, Lkv, nh)
+    else:
+        G.B.op_attention(q, k, vt, out, B, Lq, Lkv, nh)
     G.sync()
     got = G.to_f64(out)
     for b in range(B):
@@ -316,6 +319,22 @@ def test_self_attention(G, B, L, nh):
 def test_cross_attention(G, B, Lq, Lkv, nh):
     G.note(f"cross attention B={B} Lq={Lq} Lkv={Lkv} nh={nh}")
     _attn_case(G, B, Lq, Lkv, nh, False, f"ca{B}_{Lq}_{Lkv}_{nh}")
+
+
+# Key-split last round: every case below has fewer (batch, head, query-tile) units than half the CUs, so
+# all of them run as key chunks (multiples of 64 keys, the last one ragged) merged by the combine pass.
+@pytest.mark.parametrize("B,Lq,Lkv,nh,fused", [(1, 1000, 1000, 3, True), (2, 320, 320, 12, True), (1, 129, 129, 2, True),
+                                               (1, 64, 64, 1, True), (2, 300, 226, 4, False), (1, 200, 70, 2, False),
+                                               (1, 700, 1, 1, False)])
+def test_attention_key_split(G, B, Lq, Lkv, nh, fused):
+    G.note(f"attention key split B={B} Lq={Lq} Lkv={Lkv} nh={nh}")
+    _attn_case(G, B, Lq, Lkv, nh, fused, f"ks{B}_{Lq}_{Lkv}_{nh}", split=True)
+
+
+def test_attention_key_split_peaked(G):
+    """Scores in the tens with chunked keys: the merge rescales chunks whose running maxima differ."""
+    G.note("attention key split peaked")
+    _attn_case(G, 1, 500, 500, 2, True, "kspeaked", scale=3.0, split=True)
 
 
 def test_attention_peaked_scores(G):

@@ -75,12 +75,16 @@ _op_qk_norm_rope = _sig("wan_op_qk_norm_rope", [_vp, _i64, _i64, _i64, _f32, _i6
                                                 _i32, _i32, _i32, _i32, _i32, _vp])
 _op_transpose_v = _sig("wan_op_transpose_v", [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp])
 _op_attention = _sig("wan_op_attention", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp])
+_op_attention_ws = _sig("wan_op_attention_ws", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp,
+                                                _i64, _vp])
+_op_attention_ws_bytes = _sig("wan_op_attention_workspace_bytes", [], C.c_int64)
 _op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
 _probe_mfma = _sig("wan_probe_mfma", [_vp, _i32, _i64, _i32, _vp])
 
 EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
             "wan_op_patchify", "wan_op_unpatchify", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
+            "wan_op_attention_ws", "wan_op_attention_workspace_bytes",
             "wan_op_time_embed", "wan_probe_mfma"]
 
 
@@ -258,6 +262,22 @@ def op_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.
     """q, k, out: 2-D views [b*L, >= 128*nh] (row stride from the tensor); vt [b, nh, 128, ldv]."""
     _check(_op_attention(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(), vt.shape[3],
                          out.data_ptr(), out.stride(0), b, lq, lkv, nh, _stream(stream)))
+    return out
+
+
+def attention_workspace_bytes() -> int:
+    return int(_op_attention_ws_bytes())
+
+
+def op_attention_ws(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Tensor, b: int, lq: int, lkv: int,
+                    nh: int, workspace: torch.Tensor = None, stream=None):
+    """op_attention with a device workspace (allocated here when not given): the last round of
+    workgroups may be split over key chunks and merged."""
+    if workspace is None:
+        workspace = torch.empty(attention_workspace_bytes() // 4, dtype=torch.float32, device=q.device)
+    _check(_op_attention_ws(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(), vt.shape[3],
+                            out.data_ptr(), out.stride(0), b, lq, lkv, nh, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -47,6 +47,7 @@ constexpr int K_TILE_BYTES = KT * 256;     // 64 rows of 128 bf16
 constexpr int V_TILE_BYTES = 128 * KT * 2; // 128 rows of 64 bf16
 constexpr int TILE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
 constexpr float RESCALE_LOG2 = 8.0f;
+constexpr int64_t ATTN_SPLIT_MAX = 256;   // workgroups of a key-split launch (workspace size)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -59,6 +60,13 @@ struct AttnArgs {
   int nh, B;
   int q_tiles;
   float scale_log2;   // log2(e) / sqrt(128)
+  int units;          // workgroups of the regular launch: units 0 .. units-1, unit = (b, h, query tile)
+  // key-split launch: workgroup w works on unit units_base + w / split over keys
+  // [chunk (w % split), chunk (w % split + 1)) and writes unnormalised partial results
+  int split, units_base;
+  int64_t chunk;
+  float* part_o;      // [w][256 queries][128]: sum over the chunk's keys of p * v (p relative to m)
+  float* part_ml;     // [w][256 queries][2]: running max m (raw score units) and row sum l
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
@@ -186,16 +194,19 @@ __device__ __forceinline__ void pv(AttnState& st, const u32x4 (&pf)[2][2], const
 }
 
 // SELF selects the instantiation only (self- and cross-attention then show up as separate kernels in
-// a trace); the code path is the same.
-template <bool SELF>
+// a trace); the code path is the same.  PART: one key chunk of a unit, unnormalised output (see
+// AttnArgs); the last round of a launch that would leave most CUs idle is run this way.
+template <bool SELF, bool PART>
 __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TILE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   // Workgroups of one (batch, head) are kept on one XCD so they share K/V in its L2.
-  const int nb = a.q_tiles * a.nh * a.B;
-  const int lid = xcd_remap(blockIdx.x, nb);
+  const int lid = PART ? a.units_base + (int)blockIdx.x / a.split : xcd_remap(blockIdx.x, a.units);
+  const int64_t k_lo = PART ? (int64_t)((int)blockIdx.x % a.split) * a.chunk : 0;
+  // keys of this workgroup: [k_lo, k_lo + Lkv) of its (batch, head)
+  const int64_t Lkv = PART ? (a.Lkv - k_lo < a.chunk ? a.Lkv - k_lo : a.chunk) : a.Lkv;
   const int qt = lid % a.q_tiles;
   const int bh = lid / a.q_tiles;
   const int h = bh % a.nh, b = bh / a.nh;
@@ -220,10 +231,10 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   // ---- direct global -> LDS copies.  Each wave issues 4 K and 4 V instructions per tile.
   //   K: instruction I (= 4 wave + i) fills rows 4I .. 4I+3; lane -> row 4I + lane/16, position lane%16.
   //   V: instruction I fills rows 8I .. 8I+7; lane -> row 8I + lane/8, position lane%8.
-  const bf16_t* kbase = a.k + (int64_t)b * a.Lkv * a.ldk + h * 128;
-  const bf16_t* vbase = a.vt + ((int64_t)b * a.nh + h) * 128 * a.ldv;
-  const int n_tiles = (int)((a.Lkv + KT - 1) / KT);
-  const int n_sub = (int)((a.Lkv + KS - 1) / KS);
+  const bf16_t* kbase = a.k + ((int64_t)b * a.Lkv + k_lo) * a.ldk + h * 128;
+  const bf16_t* vbase = a.vt + ((int64_t)b * a.nh + h) * 128 * a.ldv + k_lo;
+  const int n_tiles = (int)((Lkv + KT - 1) / KT);
+  const int n_sub = (int)((Lkv + KS - 1) / KS);
   // per-lane byte offsets inside a tile (K rows of the tile, Vt rows), fixed for the whole loop
   uint32_t k_off[4], v_off[4];
   int k_row[4];
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     const int v_col = ((lane & 7) ^ v_swz(v_row)) * 8;
     v_off[i] = (uint32_t)(((int64_t)v_row * a.ldv + v_col) * 2);
   }
-  const bool tail_rows = (a.Lkv % KT) != 0;
+  const bool tail_rows = (Lkv % KT) != 0;
   // half 0 of tile t: its 4 K instructions; half 1: its 4 V instructions
   auto issue = [&](int t, int part) {
     const int64_t key0 = (int64_t)t * KT;
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
         // last, partial tile: rows past the end re-read the last valid row (their scores are masked)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t key = key0 + k_row[i] < a.Lkv ? k_row[i] : a.Lkv - 1 - key0;
+          const int64_t key = key0 + k_row[i] < Lkv ? k_row[i] : Lkv - 1 - key0;
           const uint32_t off = (uint32_t)(k_off[i] + (key - k_row[i]) * a.ldk * 2);
           __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void*)(lk + (4 * wave + i) * 1024), 16, 0, 0);
         }
@@ -276,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   }
   const float c = a.scale_log2;
   const float grow_thr = RESCALE_LOG2 / c;   // raw-score margin before the max is raised
-  const int last_lim = (int)(a.Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
+  const int last_lim = (int)(Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
 
   // vmcnt(n) for n in {0, 4, 8, 12, 16}, with or without lgkmcnt(0)
   auto wait_vm = [&](int n, auto lgkm0) {
@@ -357,6 +368,18 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32, 64);
+    if constexpr (PART) {
+      const int qloc = wave * QWAVE + qb * 32 + l32;
+      float* po = a.part_o + ((int64_t)blockIdx.x * QB + qloc) * 128 + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg)
+          *(f32x4*)(po + 32 * dt + 8 * rg) = (f32x4){st.o[qb][dt][4 * rg], st.o[qb][dt][4 * rg + 1],
+                                                     st.o[qb][dt][4 * rg + 2], st.o[qb][dt][4 * rg + 3]};
+      if (g == 0) *(f32x2*)(a.part_ml + ((int64_t)blockIdx.x * QB + qloc) * 2) = (f32x2){st.m_run[qb], l_tot};
+      continue;
+    }
     const float inv = 1.0f / l_tot;
     if (qi[qb] < a.Lq) {
       bf16_t* op = a.o + ((int64_t)b * a.Lq + qi[qb]) * a.ldo + h * 128 + 4 * g;
@@ -373,11 +396,37 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   }
 }
 
+// Merge of the key chunks of the split units: per query, m = max_c m_c, w_c = 2^((m_c - m) log2(e)/sqrt(128)),
+// O = (sum_c w_c O_c) / (sum_c w_c l_c): the softmax over all keys, exactly as one pass would form it.
+// One 256-thread workgroup per (unit, 2 queries), one thread per output element.
+__global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
+  const int tu = (int)blockIdx.x / (QB / 2);
+  const int q = ((int)blockIdx.x % (QB / 2)) * 2 + (int)(threadIdx.x >> 7), d = (int)threadIdx.x & 127;
+  const int lid = a.units_base + tu;
+  const int qt = lid % a.q_tiles, bh = lid / a.q_tiles;
+  const int h = bh % a.nh, b = bh / a.nh;
+  const int64_t qi = (int64_t)qt * QB + q;
+  if (qi >= a.Lq) return;
+  const int64_t w0 = (int64_t)tu * a.split;
+  float m = -INFINITY;
+  for (int c = 0; c < a.split; ++c) m = fmaxf(m, a.part_ml[((w0 + c) * QB + q) * 2]);
+  float l = 0.f, acc = 0.f;
+  for (int c = 0; c < a.split; ++c) {
+    const int64_t r = (w0 + c) * QB + q;
+    const float w = __builtin_amdgcn_exp2f((a.part_ml[r * 2] - m) * a.scale_log2);
+    l = fmaf(a.part_ml[r * 2 + 1], w, l);
+    acc = fmaf(a.part_o[r * 128 + d], w, acc);
+  }
+  a.o[((int64_t)b * a.Lq + qi) * a.ldo + h * 128 + d] = (bf16_t)(pack_bf16x2(acc / l, 0.f) & 0xFFFFu);
+}
+
 }  // namespace
+
+int64_t attention_workspace_bytes() { return (int64_t)ATTN_SPLIT_MAX * QB * (128 + 2) * 4; }
 
 hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
                             bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, bool self_attn,
-                            hipStream_t s) {
+                            hipStream_t s, float* ws, int64_t ws_bytes) {
   if (B <= 0 || Lq <= 0) return hipSuccess;
   if (Lkv <= 0 || ldv < round_up(Lkv, KT)) return hipErrorInvalidValue;
   AttnArgs a;
@@ -385,9 +434,40 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
   a.Lq = Lq; a.Lkv = Lkv; a.nh = nh; a.B = (int)B;
   a.q_tiles = (int)ceil_div(Lq, QB);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
-  const int64_t nb = (int64_t)a.q_tiles * nh * B;
-  if (self_attn) hipLaunchKernelGGL(k_flash_attn<true>, dim3((unsigned)nb), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_flash_attn<false>, dim3((unsigned)nb), dim3(256), 0, s, a);
+  a.split = 1; a.units_base = 0; a.chunk = Lkv; a.part_o = nullptr; a.part_ml = nullptr;
+  const int64_t units = (int64_t)a.q_tiles * nh * B;
+  // One workgroup per CU at a time: the last round holds units % CUs workgroups.  When it is at most half
+  // full, its units are split over key chunks (multiples of 64 keys) so that it fills the chip, and a
+  // merge pass forms their outputs.
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      n_cu = v;
+    if (n_cu <= 0) n_cu = 256;
+  }
+  const int64_t tail = units % n_cu;
+  int64_t split = 1, chunk = Lkv;
+  if (ws != nullptr && tail > 0 && 2 * tail <= n_cu) {
+    chunk = round_up(ceil_div(Lkv, n_cu / tail), KT);
+    split = ceil_div(Lkv, chunk);
+    if (split < 2 || tail * split > ATTN_SPLIT_MAX || ws_bytes < attention_workspace_bytes()) split = 1;
+  }
+  auto launch = [&](auto self_tag, auto part_tag, int64_t grid) {
+    constexpr bool SELF = decltype(self_tag)::value, PART = decltype(part_tag)::value;
+    if (grid > 0) hipLaunchKernelGGL((k_flash_attn<SELF, PART>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  a.units = (int)(split > 1 ? units - tail : units);
+  if (self_attn) launch(T{}, F{}, a.units);
+  else launch(F{}, F{}, a.units);
+  if (split > 1) {
+    a.split = (int)split; a.units_base = a.units; a.chunk = chunk;
+    a.part_o = ws; a.part_ml = ws + (int64_t)ATTN_SPLIT_MAX * QB * 128;
+    if (self_attn) launch(T{}, T{}, tail * split);
+    else launch(F{}, T{}, tail * split);
+    hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(tail * (QB / 2))), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
-

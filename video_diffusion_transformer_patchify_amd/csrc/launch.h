@@ -35,8 +35,11 @@ int64_t rope_table_floats(int Fp, int Hp, int Wp, int dt, int dh, int dw);
 hipError_t launch_rope_table(float* tab, int Fp, int Hp, int Wp, int dt, int dh, int dw, double theta, hipStream_t s);
 hipError_t launch_sinusoid(const float* t, int64_t rows, int freq_dim, float* out, hipStream_t s);
 
+// ws (attention_workspace_bytes() bytes, or null): lets a launch whose last round of workgroups would
+// leave most CUs idle split that round over key chunks and merge them (same result up to fp32 rounding)
 hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
                             bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, bool self_attn,
-                            hipStream_t s);
+                            hipStream_t s, float* ws = nullptr, int64_t ws_bytes = 0);
+int64_t attention_workspace_bytes();
 
 hipError_t launch_mfma_probe(float* sink, int blocks, int64_t rounds, int random_operands, hipStream_t s);

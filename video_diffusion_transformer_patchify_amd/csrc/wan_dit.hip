@@ -82,6 +82,7 @@ struct wan_dit {
   // workspace
   bf16_t *P, *y, *qkv, *vt, *attn, *br, *hbuf, *text_bf, *ctx_h, *ctx, *kv2, *vt2;
   float *x, *z, *t_s, *t_h, *temb, *tproj, *rope;
+  float* attn_ws;   // key-split partials of the attention's last round
   int64_t ldv_max, ldv2_max, rows_max, trows_max;
 };
 
@@ -222,6 +223,7 @@ void plan_workspace(wan_dit* h, Arena& ar) {
   h->ctx = ar.take<bf16_t>(Tx * D);
   h->kv2 = ar.take<bf16_t>(Tx * 2 * D);
   h->vt2 = ar.take<bf16_t>(c.max_batch * D * h->ldv2_max);
+  h->attn_ws = ar.take<float>(attention_workspace_bytes() / 4);
 }
 
 void free_handle(wan_dit* h) {
@@ -465,7 +467,8 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
     HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, s),
             "qk norm rope");
     HIP_TRY(launch_transpose_v(h->qkv, 3 * D, 2 * D, B, L, (int)nh, h->vt, ldv, s), "v transpose");
-    HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s), "self attention");
+    HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s,
+                             h->attn_ws, attention_workspace_bytes()), "self attention");
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn1 out");
     // cross-attention: x += gate1 * attn, then norm2 (affine)
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 1, nullptr, nullptr, nullptr, 0, 0, 0, rows_per_mod, b.n2w, b.n2b, 2, h->br,
@@ -477,7 +480,8 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
             "kv2");
     HIP_TRY(launch_rms_rope(h->kv2, 2 * D, B * Lt, D, eps, 0, b.gk2, 0, nullptr, nullptr, Lt, 1, 1, 1, dt, dh, dw, s), "k2 norm");
     HIP_TRY(launch_transpose_v(h->kv2, 2 * D, D, B, Lt, (int)nh, h->vt2, ldv2, s), "v2 transpose");
-    HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, false, s), "cross attention");
+    HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, false, s,
+                             h->attn_ws, attention_workspace_bytes()), "cross attention");
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn2 out");
     // feed-forward: x += cross-attn (ungated), then norm3 + modulation
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 3 * D, b.table + 4 * D, h->tproj, 6 * D, 3 * D, 4 * D,
@@ -629,6 +633,26 @@ extern "C" wan_status wan_op_attention(const void* q, int64_t ldq, const void* k
   REQUIRE((q && k && vt && o) || B * Lq == 0, WAN_ERR_INVALID_ARG, "attention: NULL pointer");
   HIP_TRY(launch_attention((const bf16_t*)q, ldq, (const bf16_t*)k, ldk, (const bf16_t*)vt, ldv, (bf16_t*)o, ldo, B, Lq, Lkv, nh,
                            Lq == Lkv, (hipStream_t)stream), "attention");
+  return WAN_OK;
+}
+
+extern "C" int64_t wan_op_attention_workspace_bytes(void) { return attention_workspace_bytes(); }
+
+extern "C" wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
+                                          int64_t ldv, void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh,
+                                          void* workspace, int64_t workspace_bytes, void* stream) {
+  g_err.clear();
+  REQUIRE(B >= 0 && Lq >= 0 && nh > 0, WAN_ERR_SHAPE, "attention: bad sizes");
+  REQUIRE(Lkv >= 1 || B * Lq == 0, WAN_ERR_SHAPE, "attention: at least one key is needed");
+  REQUIRE(ldv % 64 == 0 && ldv >= Lkv, WAN_ERR_SHAPE, "attention: ldv must be a multiple of 64 and >= Lkv");
+  REQUIRE(ldq % 8 == 0 && ldk % 8 == 0 && ldo % 4 == 0 && ldq >= 128LL * nh && ldk >= 128LL * nh && ldo >= 128LL * nh,
+          WAN_ERR_SHAPE, "attention: bad row strides");
+  REQUIRE((q && k && vt && o) || B * Lq == 0, WAN_ERR_INVALID_ARG, "attention: NULL pointer");
+  REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 15) == 0 && workspace_bytes >= attention_workspace_bytes(),
+          WAN_ERR_INVALID_ARG, "attention: workspace must be 16-byte aligned and >= %lld bytes",
+          (long long)attention_workspace_bytes());
+  HIP_TRY(launch_attention((const bf16_t*)q, ldq, (const bf16_t*)k, ldk, (const bf16_t*)vt, ldv, (bf16_t*)o, ldo, B, Lq, Lkv, nh,
+                           Lq == Lkv, (hipStream_t)stream, (float*)workspace, workspace_bytes), "attention");
   return WAN_OK;
 }
 
