@@ -200,7 +200,9 @@ template <bool SELF, bool PART>
 __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TILE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: held in a scalar register, every direct load's LDS address (M0) is
+  // scalar arithmetic instead of a vector add and a readfirstlane per load
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   // Workgroups of one (batch, head) are kept on one XCD so they share K/V in its L2.
   const int lid = PART ? a.units_base + (int)blockIdx.x / a.split : xcd_remap(blockIdx.x, a.units);
