@@ -84,6 +84,7 @@ __device__ __forceinline__ int v_swz(int r) { return ((r >> 1) ^ (r << 2)) & 7; 
 struct AttnState {
   f32x16 o[2][4];
   float m_run[2], l_run[2];
+  float mc[2];   // -m_run * c, the exponent offset of the probabilities
 };
 
 // S^T for sub-tile `sub` (0 or 1) of an LDS tile, both query blocks; each K fragment read once.
@@ -143,6 +144,7 @@ __device__ __forceinline__ void maybe_rescale(AttnState& st, const float (&mx)[2
       const float m_new = grow ? mx[qb] : st.m_run[qb];
       const float alpha = __builtin_amdgcn_exp2f((st.m_run[qb] - m_new) * c);
       st.m_run[qb] = m_new;
+      st.mc[qb] = -m_new * c;
       st.l_run[qb] *= alpha;
       // one 16-register accumulator at a time: they live in AGPRs, each multiply needs VGPR temporaries
 #pragma unroll
@@ -158,15 +160,15 @@ __device__ __forceinline__ void maybe_rescale(AttnState& st, const float (&mx)[2
 __device__ __forceinline__ void probs(AttnState& st, const f32x16 (&s)[2], u32x4 (&pf)[2][2], float c) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float mc = -st.m_run[qb] * c;
-    float ls = 0.f;
+    const float mc = st.mc[qb];
+    float ls;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], c, mc));
-        ls += p[e];
+        ls = (hh == 0 && e == 0) ? p[e] : ls + p[e];
       }
       u32x4 w;
       w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]);
@@ -285,6 +287,7 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.o[qb][i] = (f32x16){};
     st.m_run[qb] = -INFINITY;
+    st.mc[qb] = INFINITY;
     st.l_run[qb] = 0.f;
   }
   const float c = a.scale_log2;
