@@ -355,6 +355,25 @@ def test_self_attention_full_size_sampled(G):
 # ------------------------------------------------------------------------------------------------
 
 
+# Key counts around the 64-key LDS tile and the 32-key sub-tile, query counts around the 256-query
+# workgroup; each through the plain entry point and through the one with a workspace, which splits
+# these small launches into 64-key chunks (65 keys: a last chunk of one key).
+_EDGE_CASES = [
+    (1, 31, 31, 1, True), (1, 33, 33, 1, True), (1, 63, 63, 1, True), (1, 65, 65, 1, True),
+    (1, 96, 96, 1, True), (1, 127, 127, 1, True), (1, 255, 255, 1, True), (1, 257, 257, 1, True),
+    (2, 256, 256, 1, True), (1, 513, 513, 1, True),
+    (1, 255, 2, 1, False), (1, 257, 32, 1, False), (2, 100, 33, 2, False), (1, 300, 95, 1, False),
+    (1, 40, 97, 1, False), (1, 512, 321, 1, False), (1, 1, 129, 1, False),
+]
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_attention_tile_edges(G, split):
+    for i, (B, Lq, Lkv, nh, fused) in enumerate(_EDGE_CASES):
+        G.note(f"attention edge case B={B} Lq={Lq} Lkv={Lkv} nh={nh} fused={fused} split={split}")
+        _attn_case(G, B, Lq, Lkv, nh, fused, f"edge{i}", split=split)
+
+
 @pytest.mark.parametrize("rows,D,per_token", [(2, 1536, False), (1, 5120, False), (2000, 3072, True)])
 def test_time_embed(G, rows, D, per_token):
     import torch
