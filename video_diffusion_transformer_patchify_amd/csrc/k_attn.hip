@@ -444,13 +444,11 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
   // One workgroup per CU at a time: the last round holds units % CUs workgroups.  When it is at most half
   // full, its units are split over key chunks (multiples of 64 keys) so that it fills the chip, and a
   // merge pass forms their outputs.
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      n_cu = v;
-    if (n_cu <= 0) n_cu = 256;
-  }
+  // CUs of the current device, asked per launch (the runtime keeps device attributes; devices may differ)
+  int n_cu = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu <= 0)
+    n_cu = 256;
   const int64_t tail = units % n_cu;
   int64_t split = 1, chunk = Lkv;
   if (ws != nullptr && tail > 0 && 2 * tail <= n_cu) {
