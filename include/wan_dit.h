@@ -122,6 +122,22 @@ wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, const wan_tenso
 /* Release the handle's device buffers.  NULL is ignored. */
 void wan_dit_destroy(wan_dit* h);
 
+/* Opt-in timing of the self-attention kernel inside wan_dit_forward, for benchmarks (not part of the
+ * computation: the softmax(Q K^T / sqrt(128)) V of every block runs the same either way).
+ * max_launches > 0 creates 2 * max_launches HIP events on the handle's device, owned by the handle; every
+ * later self-attention launch of wan_dit_forward is then bracketed by an event pair recorded on the
+ * forward's stream, until max_launches pairs are in use (later launches run untimed).  max_launches == 0
+ * turns the timing off and releases the events; wan_dit_destroy releases them too.  The forward still
+ * allocates nothing.  Errors: WAN_ERR_INVALID_ARG (NULL handle, max_launches outside [0, 2^20], current
+ * device not the handle's), WAN_ERR_HIP (event creation failed; no events are kept). */
+wan_status wan_dit_time_attention(wan_dit* h, int64_t max_launches);
+
+/* Sum in milliseconds of the self-attention launches timed since the last call (or since
+ * wan_dit_time_attention), and their number.  Host-synchronous: waits for the recorded events.  The
+ * event pairs are free for reuse afterwards.  Errors: WAN_ERR_INVALID_ARG (NULL handle or output
+ * pointer, current device not the handle's), WAN_ERR_HIP (an event query failed). */
+wan_status wan_dit_attention_time(wan_dit* h, double* total_ms, int64_t* launches);
+
 /* Text of the last error on the calling thread ("" if none); valid until the next call. */
 const char* wan_dit_last_error(void);
 

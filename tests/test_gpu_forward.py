@@ -104,6 +104,36 @@ def test_determinism_and_batch_duplicates(G):
     assert np.array_equal(b1[0], b1[1])            # duplicated batch element
 
 
+def test_attention_timing(G):
+    """wan_dit_time_attention / wan_dit_attention_time: one timed launch per block and forward up to the
+    requested count, a reset after each query, timing off at 0, and the same output with and without."""
+    import torch
+
+    G.note("attention timing entry points")
+    cfg = get_config(2).replace(num_layers=3, frames=3, height=16, width=16, text_len=64)
+    w = Weights(cfg)
+    lat, t, txt = draw_inputs(cfg)
+    model, out0 = run_gpu(G, cfg, w, lat, t, txt)
+    args = (G.to_device(lat), G.to_device(t), G.to_device(txt))
+    model.time_attention(4)                      # room for 4 of the 6 launches of two forwards
+    out1 = model.forward(*args)
+    out2 = model.forward(*args)
+    total, n = model.attention_time()
+    assert n == 4 and total > 0.0, (n, total)
+    assert model.attention_time() == (0.0, 0)    # counted once
+    model.forward(*args)
+    total, n = model.attention_time()            # the event pairs were free again
+    assert n == 3 and total > 0.0, (n, total)
+    model.time_attention(0)
+    model.forward(*args)
+    assert model.attention_time() == (0.0, 0)
+    torch.cuda.synchronize()
+    b0 = G.bf16_bits(out0)
+    assert np.array_equal(b0, G.bf16_bits(out1)) and np.array_equal(b0, G.bf16_bits(out2))
+    with pytest.raises(G.B.WanError):
+        model.time_attention(-1)
+
+
 def test_zero_gates_block_is_identity(G):
     """Gates exactly zero (table and time_proj rows) and a zero cross-attn output projection make every
     block the identity: N blocks give the same bits as 0 blocks."""

@@ -63,6 +63,8 @@ _forward = _sig("wan_dit_forward", [_vp, C.POINTER(WanTensor), C.POINTER(WanTens
 _destroy = _sig("wan_dit_destroy", [_vp], None)
 _last_error = _sig("wan_dit_last_error", [], C.c_char_p)
 _device_bytes = _sig("wan_dit_device_bytes", [_vp], _i64)
+_time_attention = _sig("wan_dit_time_attention", [_vp, _i64])
+_attention_time = _sig("wan_dit_attention_time", [_vp, C.POINTER(C.c_double), C.POINTER(C.c_int64)])
 _op_patchify = _sig("wan_op_patchify", [_vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp])
 _op_unpatchify = _sig("wan_op_unpatchify", [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp])
 _op_gemm = _sig("wan_op_gemm", [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
@@ -82,6 +84,7 @@ _op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp
 _probe_mfma = _sig("wan_probe_mfma", [_vp, _i32, _i64, _i32, _vp])
 
 EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
+            "wan_dit_time_attention", "wan_dit_attention_time",
             "wan_op_patchify", "wan_op_unpatchify", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
             "wan_op_attention_ws", "wan_op_attention_workspace_bytes",
@@ -180,6 +183,16 @@ class WanDiT:
         lt, tt, xt, ot = (as_wan_tensor(latent), as_wan_tensor(timestep), as_wan_tensor(text), as_wan_tensor(out))
         _check(_forward(self._h, C.byref(lt), C.byref(tt), C.byref(xt), C.byref(ot), _stream(stream)))
         return out
+
+    def time_attention(self, max_launches: int):
+        """Bracket the next `max_launches` self-attention launches of forward() with HIP events (0: off)."""
+        _check(_time_attention(self._h, int(max_launches)))
+
+    def attention_time(self):
+        """(total milliseconds, launches) of the self-attention launches timed since the last call."""
+        ms, n = C.c_double(), C.c_int64()
+        _check(_attention_time(self._h, C.byref(ms), C.byref(n)))
+        return ms.value, int(n.value)
 
     def close(self):
         if getattr(self, "_h", None):

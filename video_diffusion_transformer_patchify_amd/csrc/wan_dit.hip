@@ -84,6 +84,9 @@ struct wan_dit {
   float *x, *z, *t_s, *t_h, *temb, *tproj, *rope;
   float* attn_ws;   // key-split partials of the attention's last round
   int64_t ldv_max, ldv2_max, rows_max, trows_max;
+  // opt-in timing of the self-attention launches (wan_dit_time_attention): event pairs, start then end
+  std::vector<hipEvent_t> att_ev;
+  int64_t att_used = 0;
 };
 
 namespace {
@@ -226,8 +229,15 @@ void plan_workspace(wan_dit* h, Arena& ar) {
   h->attn_ws = ar.take<float>(attention_workspace_bytes() / 4);
 }
 
+void release_events(wan_dit* h) {
+  for (hipEvent_t e : h->att_ev) (void)hipEventDestroy(e);
+  h->att_ev.clear();
+  h->att_used = 0;
+}
+
 void free_handle(wan_dit* h) {
   if (!h) return;
+  release_events(h);
   if (h->wmem) (void)hipFree(h->wmem);
   if (h->wsmem) (void)hipFree(h->wsmem);
   delete h;
@@ -254,6 +264,51 @@ extern "C" const char* wan_dit_last_error(void) { return g_err.c_str(); }
 extern "C" int64_t wan_dit_device_bytes(const wan_dit* h) { return h ? (int64_t)(h->wbytes + h->wsbytes) : 0; }
 
 extern "C" void wan_dit_destroy(wan_dit* h) { free_handle(h); }
+
+extern "C" wan_status wan_dit_time_attention(wan_dit* h, int64_t max_launches) {
+  g_err.clear();
+  if (!h) return fail(WAN_ERR_INVALID_ARG, "handle is NULL");
+  if (max_launches < 0 || max_launches > (int64_t)1 << 20)
+    return fail(WAN_ERR_INVALID_ARG, "max_launches %lld out of range [0, 2^20]", (long long)max_launches);
+  {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev), "get device");
+    if (dev != h->device) return fail(WAN_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  }
+  release_events(h);
+  h->att_ev.reserve(2 * max_launches);
+  for (int64_t i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e;
+    const hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) {
+      release_events(h);
+      return fail(WAN_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(err));
+    }
+    h->att_ev.push_back(e);
+  }
+  return WAN_OK;
+}
+
+extern "C" wan_status wan_dit_attention_time(wan_dit* h, double* total_ms, int64_t* launches) {
+  g_err.clear();
+  if (!h || !total_ms || !launches) return fail(WAN_ERR_INVALID_ARG, "handle or output pointer is NULL");
+  {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev), "get device");
+    if (dev != h->device) return fail(WAN_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  }
+  double t = 0.0;
+  for (int64_t i = 0; i < h->att_used; ++i) {
+    HIP_TRY(hipEventSynchronize(h->att_ev[2 * i + 1]), "attention timing: wait");
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, h->att_ev[2 * i], h->att_ev[2 * i + 1]), "attention timing: elapsed");
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = h->att_used;
+  h->att_used = 0;
+  return WAN_OK;
+}
 
 extern "C" wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight* weights, size_t n_weights,
                                      void* hip_stream, wan_dit** out) {
@@ -467,8 +522,11 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
     HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, s),
             "qk norm rope");
     HIP_TRY(launch_transpose_v(h->qkv, 3 * D, 2 * D, B, L, (int)nh, h->vt, ldv, s), "v transpose");
+    const bool timed = 2 * h->att_used < (int64_t)h->att_ev.size();
+    if (timed) HIP_TRY(hipEventRecord(h->att_ev[2 * h->att_used], s), "self attention timing");
     HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s,
                              h->attn_ws, attention_workspace_bytes()), "self attention");
+    if (timed) HIP_TRY(hipEventRecord(h->att_ev[2 * h->att_used++ + 1], s), "self attention timing");
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn1 out");
     // cross-attention: x += gate1 * attn, then norm2 (affine)
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 1, nullptr, nullptr, nullptr, 0, 0, 0, rows_per_mod, b.n2w, b.n2b, 2, h->br,
