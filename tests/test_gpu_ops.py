@@ -350,6 +350,17 @@ def test_self_attention_full_size_sampled(G):
     _attn_case(G, 2, 32760, 32760, 12, True, "safull", rows=rows)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("L,nh", [(75600, 40), (27280, 24)])
+def test_self_attention_largest_sampled(G, L, nh):
+    """The largest self-attention shapes (Wan-14B 720p: 75600 tokens, 40 heads, 46 rounds of workgroups and
+    64 more; TI2V-5B: 27280 tokens, 24 heads, 10 rounds and 8 more), launched with the workspace as the
+    forward launches them, so the last round runs key-split; sampled query rows against the oracle."""
+    G.note(f"self attention largest B=1 L={L} nh={nh} (key split)")
+    rows = np.unique(np.concatenate([np.arange(2), [L - 300, L - 1], np.random.default_rng(5).integers(0, L, 6)]))
+    _attn_case(G, 1, L, L, nh, True, f"salarge{L}", rows=rows, split=True)
+
+
 # ------------------------------------------------------------------------------------------------
 # timestep embedding (fp32)
 # ------------------------------------------------------------------------------------------------
