@@ -79,7 +79,9 @@ def check_against_golden(G, out, g):
     (3, None),      # I2V block stack, 36 channels, D=5120, 7920 tokens, all 4 blocks
     (4, None),      # TI2V-5B geometry, per-token timesteps, 27280 tokens, all 30 blocks
     (4, 2),         # the same workload, first 2 blocks
-    (5, 1),         # Wan-14B geometry at 720p, 75600 tokens, first block
+    # Wan-14B geometry at 720p, 75600 tokens, first block: the fp64 oracle needs more than the 64 GB of
+    # the machine that writes the stored outputs (its attention is checked on sampled rows instead)
+    pytest.param(5, 1, marks=pytest.mark.skip(reason="fp64 oracle of one 75600 x 5120 block exceeds 64 GB of host memory")),
 ])
 def test_full_size_vs_oracle(G, cfg_id, layers):
     cfg = get_config(cfg_id)
