@@ -128,8 +128,9 @@ void wan_dit_destroy(wan_dit* h);
  * later self-attention launch of wan_dit_forward is then bracketed by an event pair recorded on the
  * forward's stream, until max_launches pairs are in use (later launches run untimed).  max_launches == 0
  * turns the timing off and releases the events; wan_dit_destroy releases them too.  The forward still
- * allocates nothing.  Errors: WAN_ERR_INVALID_ARG (NULL handle, max_launches outside [0, 2^20], current
- * device not the handle's), WAN_ERR_HIP (event creation failed; no events are kept). */
+ * allocates nothing.  Call it between forwards: events of a forward still running are released by it.
+ * Errors: WAN_ERR_INVALID_ARG (NULL handle, max_launches outside [0, 2^20], current device not the
+ * handle's), WAN_ERR_HIP (event creation failed; no events are kept). */
 wan_status wan_dit_time_attention(wan_dit* h, int64_t max_launches);
 
 /* Sum in milliseconds of the self-attention launches timed since the last call (or since
