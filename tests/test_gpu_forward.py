@@ -65,6 +65,22 @@ def test_forward_two_blocks_batch2_bf16(G):
     compare(G, G.to_f64(out), ref)
 
 
+@pytest.mark.parametrize("batch,frames,height,width,text_len", [
+    (1, 1, 16, 16, 1),      # one latent frame (64 tokens) and a one-token text
+    (3, 2, 18, 22, 512),    # batch 3, 2 x 9 x 11 = 198 tokens per sample, the longest text of the workloads
+])
+def test_forward_shape_extremes(G, batch, frames, height, width, text_len):
+    """Forward against the oracle at shape extremes: a single frame, one text token, batch 3, 512 text tokens."""
+    G.note(f"forward extremes B={batch} F={frames} H={height} W={width} Lt={text_len}")
+    cfg = get_config(2).replace(num_layers=1, batch=batch, frames=frames, height=height, width=width,
+                                text_len=text_len)
+    w = Weights(cfg)
+    lat, t, txt = draw_inputs(cfg)
+    model, out = run_gpu(G, cfg, w, lat, t, txt)
+    ref = O.forward(cfg, w, lat.f64(), t.f64(), txt.f64())
+    compare(G, G.to_f64(out), ref)
+
+
 def test_forward_per_token_timesteps(G):
     """Per-token timesteps [B, L] (the TI2V-5B geometry, reduced to 1 block and 4x22x20 tokens)."""
     G.note("forward per-token timesteps")
