@@ -109,7 +109,8 @@ wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight* weights, 
                           wan_dit** out);
 
 /* One DiT forward (one denoising step's velocity prediction).
- *   latent   [B, C_in, F, H_z, W_z]  WAN_F32 or WAN_BF16; H_z, W_z even; F/2, H_z/2, W_z/2 <= 1024 grid
+ *   latent   [B, C_in, F, H_z, W_z]  WAN_F32 or WAN_BF16; H_z, W_z even; the token grid F x H_z/2 x W_z/2
+ *            has at most 1024 positions per axis (F, H_z/2, W_z/2 <= 1024: the rotary tables)
  *   timestep [B] or [B, L] WAN_F32 (integer timesteps are passed as their float values); [B, L]
  *            needs cfg.per_token_timestep, with tokens in (f, h, w) order
  *   text_emb [B, Lt, text_dim] WAN_F32 or WAN_BF16

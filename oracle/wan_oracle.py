@@ -19,12 +19,20 @@ Sources (page titles; sections / printed code):
          concatenated), 配置参数全解 (freq_dim 256, text_dim 4096, qk_norm rms_norm_across_heads, eps 1e-6,
          cross_attn_norm True, rope_max_seq_len 1024, fp32-kept modules).
 
+  [W21 6.3, 7] the flow-matching conventions: x_sigma = (1 - sigma) z + sigma eps, target velocity eps - z,
+         the Euler update x_next = x + (sigma_next - sigma) v, and the CFG combine v_u + s (v_c - v_u).
+  [W21 4]  the I2V CLIP branch: 257 image tokens of width 1280 projected to the model width by an MLP and
+         attended by a cross-attention of their own; [DIF forward] concatenates them before the text.
+
 Readings taken where the pages are silent (each one also listed in the design notes):
   sinusoid [cos, sin] with frequencies 10000^(-i/128); time MLP Lin-SiLU-Lin then SiLU-Lin(6D);
   text projection Lin-GELU_tanh-Lin; LayerNorm without affine for norm1/norm3/norm_out and with
   affine for norm2; QK RMSNorm over the whole model width with a learned gain, applied to q and k of
   both attentions, before RoPE; RoPE head-dim split 44/42/42 with theta 1e4 and adjacent pairs;
-  attention scale 1/sqrt(head_dim), no masks; every Linear/Conv has a bias.
+  attention scale 1/sqrt(head_dim), no masks; every Linear/Conv has a bias; the image MLP is
+  Lin(image_dim -> D) - GELU_tanh - Lin(D -> D) like the text projection; the image tokens, first in the
+  context, get their own key/value projections and key RMSNorm, their attention output is added to the
+  text attention output before the shared output projection.
 
 Parity status: every function here is pinned by a CPU test (closed forms, invariants, brute force or a
 torch library routine); see tests/test_oracle_pins.py.
@@ -185,6 +193,12 @@ def text_embed(e: np.ndarray, w: dict) -> np.ndarray:
     return linear(h, _arr(w, "text_embedder.linear_2.weight"), _arr(w, "text_embedder.linear_2.bias"))
 
 
+def image_embed(img: np.ndarray, w: dict) -> np.ndarray:
+    """CLIP image tokens [B, Li, image_dim] -> [B, Li, D] [W21 4: 257 tokens of 1280 through an MLP]."""
+    h = gelu_tanh(linear(img, _arr(w, "image_embedder.linear_1.weight"), _arr(w, "image_embedder.linear_1.bias")))
+    return linear(h, _arr(w, "image_embedder.linear_2.weight"), _arr(w, "image_embedder.linear_2.bias"))
+
+
 # ---------------------------------------------------------------------------------------------
 # 3D rotary embedding [ANI 架构全景 / 关键子模块: WanRotaryPosEmbed, separate 1D RoPE per T/H/W,
 # concatenated; DIF: rope table (1,1,L,64) complex for head_dim 128]
@@ -280,9 +294,36 @@ def modulation(table: np.ndarray, tproj: np.ndarray) -> list:
     return [m[:, :, i] for i in range(6)]
 
 
+def _cross_attention(y2: np.ndarray, ctx: np.ndarray, w: dict, p: str, num_heads: int, eps: float, n_img: int,
+                     workers: int) -> np.ndarray:
+    """attn2 before its output projection: text keys/values (the context after its first n_img tokens),
+    plus, with n_img > 0, an attention of its own over the leading image tokens, added."""
+    b, l, d = y2.shape
+    hd = d // num_heads
+    q2 = rms_norm(linear(y2, _arr(w, p + "attn2.to_q.weight"), _arr(w, p + "attn2.to_q.bias")), eps, _arr(w, p + "attn2.norm_q.weight"))
+    txt = ctx[:, n_img:]
+    k2 = rms_norm(linear(txt, _arr(w, p + "attn2.to_k.weight"), _arr(w, p + "attn2.to_k.bias")), eps, _arr(w, p + "attn2.norm_k.weight"))
+    v2 = linear(txt, _arr(w, p + "attn2.to_v.weight"), _arr(w, p + "attn2.to_v.bias"))
+    lt = txt.shape[1]
+    a2 = np.empty_like(q2)
+    for bi in range(b):
+        a2[bi] = attention(q2[bi].reshape(l, num_heads, hd), k2[bi].reshape(lt, num_heads, hd),
+                           v2[bi].reshape(lt, num_heads, hd), workers=workers).reshape(l, d)
+    if n_img > 0:
+        img = ctx[:, :n_img]
+        ki = rms_norm(linear(img, _arr(w, p + "attn2.add_k_proj.weight"), _arr(w, p + "attn2.add_k_proj.bias")), eps,
+                      _arr(w, p + "attn2.norm_added_k.weight"))
+        vi = linear(img, _arr(w, p + "attn2.add_v_proj.weight"), _arr(w, p + "attn2.add_v_proj.bias"))
+        for bi in range(b):
+            a2[bi] += attention(q2[bi].reshape(l, num_heads, hd), ki[bi].reshape(n_img, num_heads, hd),
+                                vi[bi].reshape(n_img, num_heads, hd), workers=workers).reshape(l, d)
+    return a2
+
+
 def block_forward(x: np.ndarray, ctx: np.ndarray, tproj: np.ndarray, ang: np.ndarray, w: dict, prefix: str,
-                  num_heads: int, eps: float = 1e-6, workers: int = 1) -> np.ndarray:
-    """One WanTransformerBlock.  x [B,L,D] (fp64), ctx [B,Lt,D], tproj [B,6,D] or [B,L,6,D]."""
+                  num_heads: int, eps: float = 1e-6, workers: int = 1, n_img: int = 0) -> np.ndarray:
+    """One WanTransformerBlock.  x [B,L,D] (fp64), ctx [B,n_img+Lt,D] (image tokens first), tproj [B,6,D] or
+    [B,L,6,D]."""
     p = prefix
     b, l, d = x.shape
     hd = d // num_heads
@@ -304,14 +345,7 @@ def block_forward(x: np.ndarray, ctx: np.ndarray, tproj: np.ndarray, ang: np.nda
 
     # 2. cross-attention (norm2 with affine; residual not gated)
     y2 = layer_norm(x, eps, _arr(w, p + "norm2.weight"), _arr(w, p + "norm2.bias"))
-    q2 = rms_norm(linear(y2, _arr(w, p + "attn2.to_q.weight"), _arr(w, p + "attn2.to_q.bias")), eps, _arr(w, p + "attn2.norm_q.weight"))
-    k2 = rms_norm(linear(ctx, _arr(w, p + "attn2.to_k.weight"), _arr(w, p + "attn2.to_k.bias")), eps, _arr(w, p + "attn2.norm_k.weight"))
-    v2 = linear(ctx, _arr(w, p + "attn2.to_v.weight"), _arr(w, p + "attn2.to_v.bias"))
-    lt = ctx.shape[1]
-    a2 = np.empty_like(q2)
-    for bi in range(b):
-        a2[bi] = attention(q2[bi].reshape(l, num_heads, hd), k2[bi].reshape(lt, num_heads, hd),
-                           v2[bi].reshape(lt, num_heads, hd), workers=workers).reshape(l, d)
+    a2 = _cross_attention(y2, ctx, w, p, num_heads, eps, n_img, workers)
     x = x + linear(a2, _arr(w, p + "attn2.to_out.weight"), _arr(w, p + "attn2.to_out.bias"))
 
     # 3. feed-forward with gated residual
@@ -319,6 +353,49 @@ def block_forward(x: np.ndarray, ctx: np.ndarray, tproj: np.ndarray, ang: np.nda
     h = gelu_tanh(linear(y3, _arr(w, p + "ffn.proj_in.weight"), _arr(w, p + "ffn.proj_in.bias")))
     x = x + linear(h, _arr(w, p + "ffn.proj_out.weight"), _arr(w, p + "ffn.proj_out.bias")) * g2
     return x
+
+
+def block_forward_rows(x: np.ndarray, ctx: np.ndarray, tproj: np.ndarray, ang: np.ndarray, w: dict, prefix: str,
+                       num_heads: int, rows, eps: float = 1e-6, workers: int = 1, n_img: int = 0) -> np.ndarray:
+    """block_forward restricted to the token rows `rows` of every batch element: [B, len(rows), D].
+
+    Only self-attention mixes tokens, and only through its keys and values, so those come from every
+    token; every other step (the queries, both attentions' outputs, the residuals, norms and FFN) is
+    evaluated on the requested rows alone.  Same arithmetic as block_forward, row by row.
+    """
+    p = prefix
+    rows = np.asarray(rows, dtype=np.int64)
+    b, l, d = x.shape
+    hd = d // num_heads
+    tp = tproj if tproj.ndim == 3 else tproj[:, rows]
+    sh1, sc1, g1, sh2, sc2, g2 = modulation(_arr(w, p + "scale_shift_table"), tp)
+    mod_all = modulation(_arr(w, p + "scale_shift_table"), tproj)
+    xr = x[:, rows]
+
+    # 1. self-attention: keys and values of all tokens, queries of the rows
+    y_all = layer_norm(x, eps) * (1.0 + mod_all[1]) + mod_all[0]
+    k = rms_norm(linear(y_all, _arr(w, p + "attn1.to_k.weight"), _arr(w, p + "attn1.to_k.bias")), eps,
+                 _arr(w, p + "attn1.norm_k.weight"))
+    v = linear(y_all, _arr(w, p + "attn1.to_v.weight"), _arr(w, p + "attn1.to_v.bias"))
+    del y_all
+    y = layer_norm(xr, eps) * (1.0 + sc1) + sh1
+    q = rms_norm(linear(y, _arr(w, p + "attn1.to_q.weight"), _arr(w, p + "attn1.to_q.bias")), eps,
+                 _arr(w, p + "attn1.norm_q.weight"))
+    a = np.empty_like(q)
+    for bi in range(b):
+        qh = apply_rope(q[bi].reshape(len(rows), num_heads, hd), ang[rows])
+        kh = apply_rope(k[bi].reshape(l, num_heads, hd), ang)
+        a[bi] = attention(qh, kh, v[bi].reshape(l, num_heads, hd), workers=workers).reshape(len(rows), d)
+    del k, v
+    xr = xr + linear(a, _arr(w, p + "attn1.to_out.weight"), _arr(w, p + "attn1.to_out.bias")) * g1
+
+    # 2. cross-attention, 3. feed-forward: per token
+    y2 = layer_norm(xr, eps, _arr(w, p + "norm2.weight"), _arr(w, p + "norm2.bias"))
+    a2 = _cross_attention(y2, ctx, w, p, num_heads, eps, n_img, workers)
+    xr = xr + linear(a2, _arr(w, p + "attn2.to_out.weight"), _arr(w, p + "attn2.to_out.bias"))
+    y3 = layer_norm(xr, eps) * (1.0 + sc2) + sh2
+    h = gelu_tanh(linear(y3, _arr(w, p + "ffn.proj_in.weight"), _arr(w, p + "ffn.proj_in.bias")))
+    return xr + linear(h, _arr(w, p + "ffn.proj_out.weight"), _arr(w, p + "ffn.proj_out.bias")) * g2
 
 
 def head_forward(x: np.ndarray, temb: np.ndarray, w: dict, eps: float = 1e-6) -> np.ndarray:
@@ -342,9 +419,19 @@ def head_forward(x: np.ndarray, temb: np.ndarray, w: dict, eps: float = 1e-6) ->
 # ---------------------------------------------------------------------------------------------
 
 
+def _context(cfg, w, text, image):
+    """Text context, with the projected image tokens concatenated in front when there are any [DIF forward]."""
+    ctx = text_embed(np.asarray(text, dtype=np.float64), w)
+    if image is None:
+        return ctx, 0
+    img = image_embed(np.asarray(image, dtype=np.float64), w)
+    return np.concatenate([img, ctx], axis=1), img.shape[1]
+
+
 def forward(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, workers: int = 1,
-            return_stages: bool = False, drop=None, checkpoint=None):
-    """latent [B,C_in,F,H_z,W_z], t [B] or [B,L], text [B,Lt,4096] -> velocity [B,C_out,F,H_z,W_z].
+            return_stages: bool = False, drop=None, checkpoint=None, image=None):
+    """latent [B,C_in,F,H_z,W_z], t [B] or [B,L], text [B,Lt,4096] (and optionally CLIP image tokens
+    [B,Li,image_dim]) -> velocity [B,C_out,F,H_z,W_z].
 
     cfg carries the geometry (dim, num_heads, num_layers, eps, rope split/theta, freq_dim, out_channels).
     weights: dict name -> array, or an object with .f64(name).  drop(prefix) is called after each block
@@ -358,7 +445,7 @@ def forward(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, w
     fp, hp, wp = token_grid(f, hz, wz, cfg.patch)
     x = patch_embed(latent, _arr(w, "patch_embedding.weight"), _arr(w, "patch_embedding.bias"))
     temb, tproj = time_embed(np.asarray(t, dtype=np.float64), w, cfg.freq_dim)
-    ctx = text_embed(np.asarray(text, dtype=np.float64), w)
+    ctx, n_img = _context(cfg, w, text, image)
     ang = rope_angles(fp, hp, wp, cfg.head_dim, cfg.rope_dims, cfg.rope_theta)
     stages = {"x0": x, "temb": temb, "tproj": tproj, "ctx": ctx, "ang": ang}
     start = 0
@@ -367,7 +454,7 @@ def forward(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, w
         if saved is not None:
             start, x = saved
     for kb in range(start, cfg.num_layers):
-        x = block_forward(x, ctx, tproj, ang, w, f"blocks.{kb}.", cfg.num_heads, cfg.eps, workers)
+        x = block_forward(x, ctx, tproj, ang, w, f"blocks.{kb}.", cfg.num_heads, cfg.eps, workers, n_img)
         if checkpoint is not None and kb + 1 < cfg.num_layers:
             checkpoint.save(kb + 1, x)
         if drop is not None:
@@ -378,3 +465,70 @@ def forward(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, w
         stages.update({"x_final": x, "z": z})
         return out, stages
     return out
+
+
+def forward_rows(cfg, weights, latent: np.ndarray, t: np.ndarray, text: np.ndarray, rows, workers: int = 1,
+                 image=None):
+    """The forward's outputs of the token rows `rows` (same for every batch element), for a stack whose
+    last block is the only one: z [B, len(rows), pt*ph*pw*C_out], the proj_out values of those tokens
+    (unpatchify scatters token n's values to out[b, c, f, 2h+i, 2w+j]).
+
+    Everything before the block runs on all tokens; the block runs through block_forward_rows; the
+    head is per token.
+    """
+    if cfg.num_layers != 1:
+        raise ValueError("forward_rows evaluates one-block stacks")
+    w = weights
+    rows = np.asarray(rows, dtype=np.int64)
+    latent = np.asarray(latent, dtype=np.float64)
+    b, _, f, hz, wz = latent.shape
+    fp, hp, wp = token_grid(f, hz, wz, cfg.patch)
+    x = patch_embed(latent, _arr(w, "patch_embedding.weight"), _arr(w, "patch_embedding.bias"))
+    temb, tproj = time_embed(np.asarray(t, dtype=np.float64), w, cfg.freq_dim)
+    ctx, n_img = _context(cfg, w, text, image)
+    ang = rope_angles(fp, hp, wp, cfg.head_dim, cfg.rope_dims, cfg.rope_theta)
+    xr = block_forward_rows(x, ctx, tproj, ang, w, "blocks.0.", cfg.num_heads, rows, cfg.eps, workers, n_img)
+    del x
+    return head_forward(xr, temb if temb.ndim == 2 else temb[:, rows], w, cfg.eps)
+
+
+# ---------------------------------------------------------------------------------------------
+# Denoising step around the forward [W21 6.3 hand-worked example, 7 inference: Euler update, CFG]
+# ---------------------------------------------------------------------------------------------
+
+
+def flow_noisy(z, eps, sigma):
+    """The noised latent at noise level sigma: (1 - sigma) z + sigma eps."""
+    return (1.0 - sigma) * np.asarray(z, dtype=np.float64) + sigma * np.asarray(eps, dtype=np.float64)
+
+
+def flow_velocity(z, eps):
+    """The velocity the DiT is trained to predict: eps - z (constant along the straight path)."""
+    return np.asarray(eps, dtype=np.float64) - np.asarray(z, dtype=np.float64)
+
+
+def cfg_combine(v_cond, v_uncond, scale):
+    """Classifier-free guidance: v_u + s (v_c - v_u)."""
+    v_u = np.asarray(v_uncond, dtype=np.float64)
+    return v_u + scale * (np.asarray(v_cond, dtype=np.float64) - v_u)
+
+
+def euler_step(x, v, sigma, sigma_next):
+    """One Euler step of the flow ODE from sigma to sigma_next: x + (sigma_next - sigma) v."""
+    return np.asarray(x, dtype=np.float64) + (sigma_next - sigma) * np.asarray(v, dtype=np.float64)
+
+
+def denoise_step(cfg, weights, latent: np.ndarray, t, text_pair: np.ndarray, scale: float, sigma: float,
+                 sigma_next: float, workers: int = 1, image=None):
+    """One guided denoising step: the batch-2 forward of the same latent [1, C_in, F, H_z, W_z] under the
+    conditional and the unconditional text (text_pair [2, Lt, 4096], conditional first; t [1] or [1, L]),
+    CFG-combined and Euler-stepped.  The first C_out channels of the latent are the noisy sample x;
+    returns x + (sigma_next - sigma) (v_u + s (v_c - v_u)) [1, C_out, F, H_z, W_z]."""
+    latent = np.asarray(latent, dtype=np.float64)
+    lat2 = np.concatenate([latent, latent], axis=0)
+    t = np.asarray(t, dtype=np.float64)
+    t2 = np.concatenate([t, t], axis=0)
+    img2 = None if image is None else np.concatenate([image, image], axis=0)
+    v = forward(cfg, weights, lat2, t2, text_pair, workers=workers, image=img2)
+    x = latent[:, :cfg.out_channels]
+    return euler_step(x, cfg_combine(v[:1], v[1:], scale), sigma, sigma_next)

@@ -458,3 +458,266 @@ def test_embedder_bias_only_paths():
     assert tproj.shape == (1, 6, d) and not np.allclose(tproj[0], b_tp)
     ctx = O.text_embed(np.random.default_rng(0).standard_normal((1, 5, cfg.text_dim)), w)
     assert np.array_equal(ctx[0], np.broadcast_to(w.f64("text_embedder.linear_2.bias"), (5, d)))
+
+
+# ------------------------------------------------------------------------------------------------
+# Time and text embedders against torch's own layers, with non-zero weights (the Linear / SiLU /
+# GELU composition is the reading; a dropped or misplaced activation changes the result)
+# ------------------------------------------------------------------------------------------------
+
+
+def _rand_weights(cfg, names, seed):
+    w = Weights(cfg)
+    rng = np.random.default_rng(seed)
+    for n in names:
+        w.set(n, rng.standard_normal(w.shape(n)) * 0.3)
+    return w
+
+
+def test_time_embed_against_torch_composition():
+    cfg = tiny_cfg()
+    names = [f"{m}.{k}" for m in ("time_embedder.linear_1", "time_embedder.linear_2", "time_proj")
+             for k in ("weight", "bias")]
+    w = _rand_weights(cfg, names, 21)
+    t = np.array([0.0, 3.5, 500.0, 999.0])
+    temb, tproj = O.time_embed(t, w, cfg.freq_dim)
+    T = lambda n: torch.from_numpy(w.f64(n))  # noqa: E731
+    half = cfg.freq_dim // 2
+    freqs = torch.exp(-math.log(10000.0) * torch.arange(half, dtype=torch.float64) / half)
+    arg = torch.from_numpy(t)[:, None] * freqs[None]
+    s = torch.cat([torch.cos(arg), torch.sin(arg)], dim=-1)
+    h = F.silu(F.linear(s, T("time_embedder.linear_1.weight"), T("time_embedder.linear_1.bias")))
+    te = F.linear(h, T("time_embedder.linear_2.weight"), T("time_embedder.linear_2.bias"))
+    tp = F.linear(F.silu(te), T("time_proj.weight"), T("time_proj.bias")).unflatten(1, (6, cfg.dim))
+    assert np.abs(temb - te.numpy()).max() <= 1e-12 * max(1.0, np.abs(temb).max())
+    assert np.abs(tproj - tp.numpy()).max() <= 1e-12 * max(1.0, np.abs(tproj).max())
+    # without the inner SiLU, or without the one before time_proj, the values differ clearly
+    te_nosilu = F.linear(F.linear(s, T("time_embedder.linear_1.weight"), T("time_embedder.linear_1.bias")),
+                         T("time_embedder.linear_2.weight"), T("time_embedder.linear_2.bias"))
+    assert np.abs(temb - te_nosilu.numpy()).max() > 1e-3
+
+
+def test_text_embed_against_torch_composition():
+    cfg = tiny_cfg()
+    names = [f"text_embedder.linear_{i}.{k}" for i in (1, 2) for k in ("weight", "bias")]
+    w = _rand_weights(cfg, names, 22)
+    e = np.random.default_rng(23).standard_normal((2, 5, cfg.text_dim))
+    got = O.text_embed(e, w)
+    T = lambda n: torch.from_numpy(w.f64(n))  # noqa: E731
+    h = F.gelu(F.linear(torch.from_numpy(e), T("text_embedder.linear_1.weight"), T("text_embedder.linear_1.bias")),
+               approximate="tanh")
+    ref = F.linear(h, T("text_embedder.linear_2.weight"), T("text_embedder.linear_2.bias")).numpy()
+    assert np.abs(got - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    h_erf = F.gelu(F.linear(torch.from_numpy(e), T("text_embedder.linear_1.weight"), T("text_embedder.linear_1.bias")))
+    ref_erf = F.linear(h_erf, T("text_embedder.linear_2.weight"), T("text_embedder.linear_2.bias")).numpy()
+    assert np.abs(got - ref_erf).max() > 1e-6                     # the tanh form, not the erf one
+
+
+# ------------------------------------------------------------------------------------------------
+# Per-token timesteps through the whole forward (time MLP, modulation and head per token)
+# ------------------------------------------------------------------------------------------------
+
+
+def test_forward_per_token_timesteps_equal_broadcast():
+    cfg = tiny_cfg(batch=2)
+    w = Weights(cfg)
+    lat, _, txt = draw_inputs(cfg)
+    t_b = np.array([500.0, 137.0])
+    out_b = O.forward(cfg, w, lat.f64(), t_b, txt.f64())
+    t_tok = np.repeat(t_b[:, None], cfg.tokens, axis=1)
+    out_tok = O.forward(cfg.replace(per_token_t=True), w, lat.f64(), t_tok, txt.f64())
+    assert np.abs(out_tok - out_b).max() <= 1e-12 * np.abs(out_b).max()
+    # and a token's own timestep matters: changing one token's t changes that token's output
+    t_tok[0, 5] = 900.0
+    out_one = O.forward(cfg.replace(per_token_t=True), w, lat.f64(), t_tok, txt.f64())
+    assert np.abs(out_one - out_b).max() > 1e-3
+
+
+def test_head_per_token_equal_rows_match_per_sample():
+    cfg = tiny_cfg()
+    w = Weights(cfg)
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((2, cfg.tokens, cfg.dim))
+    temb = rng.standard_normal((2, cfg.dim))
+    z2 = O.head_forward(x, temb, w)
+    z3 = O.head_forward(x, np.repeat(temb[:, None], cfg.tokens, axis=1), w)
+    assert np.abs(z3 - z2).max() <= 1e-13 * np.abs(z2).max()
+
+
+# ------------------------------------------------------------------------------------------------
+# Denoising step: the hand-worked flow-matching example and the CFG combine
+# ------------------------------------------------------------------------------------------------
+
+
+def test_flow_matching_worked_example():
+    e = GOLDEN["flow_matching_example"]
+    z, eps, sigma = e["z"], e["eps"], e["sigma"]
+    x = O.flow_noisy(z, eps, sigma)
+    assert x == e["x_sigma"]
+    v = O.flow_velocity(z, eps)
+    assert v == e["v_target"]
+    assert (7.0 - v) ** 2 == 1.0                         # the printed squared error of a prediction of 7
+    x1 = O.euler_step(x, v, sigma, 0.5)
+    assert x1 == e["step_to_0p5"]
+    assert O.euler_step(x1, v, 0.5, 0.0) == e["step_to_0"] == z   # the straight path lands on the data
+    # stepping with the exact velocity from any sigma reaches the same point
+    for s0, s1 in [(1.0, 0.25), (0.9, 0.3)]:
+        assert abs(O.euler_step(O.flow_noisy(z, eps, s0), v, s0, s1) - O.flow_noisy(z, eps, s1)) < 1e-14
+
+
+def test_cfg_combine_special_cases():
+    rng = np.random.default_rng(25)
+    vc, vu = rng.standard_normal((2, 3, 4, 5))
+    assert np.allclose(O.cfg_combine(vc, vu, 1.0), vc, rtol=0, atol=1e-15)   # v_u + (v_c - v_u): one rounding
+    assert np.array_equal(O.cfg_combine(vc, vu, 0.0), vu)
+    assert np.allclose(O.cfg_combine(vc, vc, 6.0), vc, rtol=0, atol=1e-15)
+    s = 6.0
+    g = O.cfg_combine(vc, vu, s)
+    assert np.allclose(g - vu, s * (vc - vu), rtol=1e-14, atol=1e-14)   # extrapolation along v_c - v_u
+    assert np.allclose(O.cfg_combine(vc, vu, 2.0), 2 * vc - vu, rtol=1e-14, atol=1e-14)
+
+
+def test_denoise_step_is_forward_then_cfg_then_euler():
+    cfg = tiny_cfg(batch=2)
+    w = Weights(cfg)
+    lat, _, txt = draw_inputs(cfg.replace(batch=1))
+    text_pair = np.random.default_rng(26).standard_normal((2, cfg.text_len, cfg.text_dim))
+    lat1 = lat.f64()
+    got = O.denoise_step(cfg, w, lat1, np.array([750.0]), text_pair, 5.0, 0.75, 0.5)
+    v = O.forward(cfg, w, np.concatenate([lat1, lat1]), np.array([750.0, 750.0]), text_pair)
+    ref = lat1[:, :cfg.out_channels] + (0.5 - 0.75) * (v[1:] + 5.0 * (v[:1] - v[1:]))
+    assert np.abs(got - ref).max() <= 1e-13 * np.abs(ref).max()
+    # the unconditional text only acts through the guidance: with s = 1 it drops out
+    one = O.denoise_step(cfg, w, lat1, np.array([750.0]), text_pair, 1.0, 0.75, 0.5)
+    other = text_pair.copy()
+    other[1] = 0.0
+    assert np.allclose(O.denoise_step(cfg, w, lat1, np.array([750.0]), other, 1.0, 0.75, 0.5), one,
+                       rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------
+# I2V image branch: projected CLIP tokens first in the context, attended by their own keys/values
+# ------------------------------------------------------------------------------------------------
+
+
+def _i2v_cfg(**kw):
+    base = dict(image_len=5, image_dim=12)
+    base.update(kw)
+    return tiny_cfg(**base)
+
+
+def test_image_embed_shape_printed():
+    e = GOLDEN["i2v_image_tokens"]
+    cfg = get_config(3).replace(image_len=e["tokens"], num_layers=0)
+    assert (cfg.image_len, cfg.image_dim, cfg.dim) == (e["tokens"], e["image_dim"], e["projected_dim"])
+    assert cfg.in_channels == e["latent_channels"]["total"] == sum(
+        e["latent_channels"][k] for k in ("noise", "condition", "mask"))
+    w = Weights(cfg)
+    img = np.random.default_rng(27).standard_normal((1, e["tokens"], e["image_dim"]))
+    assert O.image_embed(img, w).shape == (1, e["tokens"], e["projected_dim"])
+
+
+def test_image_branch_against_torch_composition():
+    cfg = _i2v_cfg(batch=2)
+    w, x, _, tproj, ang = _block_setup(cfg)
+    rng = np.random.default_rng(28)
+    ctx = rng.standard_normal((2, cfg.image_len + cfg.text_len, cfg.dim))
+    got = O.block_forward(x, ctx, tproj, ang, w, "blocks.0.", cfg.num_heads, cfg.eps, n_img=cfg.image_len)
+    # the block without image tokens plus the image attention's contribution, through torch
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    W = lambda n: T(w.f64("blocks.0." + n))  # noqa: E731
+    d, nh = cfg.dim, cfg.num_heads
+    hd = d // nh
+    heads = lambda u: u.unflatten(-1, (nh, hd)).transpose(1, 2)  # noqa: E731
+    y2_fn = lambda xx: F.layer_norm(xx, (d,), W("norm2.weight"), W("norm2.bias"), cfg.eps)  # noqa: E731
+    # x after the self-attention step, computed with the oracle's own first half (the text-only block
+    # with zero cross output gives it), then the cross step in torch with both key sets
+    w0 = Weights(cfg)
+    for n in w.names():
+        w0.set(n, w.f64(n))
+    w0.set("blocks.0.attn2.to_out.weight", np.zeros((d, d)))
+    w0.set("blocks.0.attn2.to_out.bias", np.zeros(d))
+    w0.set("blocks.0.ffn.proj_out.weight", np.zeros((d, cfg.ffn_dim)))
+    w0.set("blocks.0.ffn.proj_out.bias", np.zeros(d))
+    x1 = T(O.block_forward(x, ctx[:, cfg.image_len:], tproj, ang, w0, "blocks.0.", nh, cfg.eps))
+    y2 = y2_fn(x1)
+    q2 = F.rms_norm(F.linear(y2, W("attn2.to_q.weight"), W("attn2.to_q.bias")), (d,), W("attn2.norm_q.weight"), cfg.eps)
+    ct = T(ctx)
+    img, txt = ct[:, :cfg.image_len], ct[:, cfg.image_len:]
+    k2 = F.rms_norm(F.linear(txt, W("attn2.to_k.weight"), W("attn2.to_k.bias")), (d,), W("attn2.norm_k.weight"), cfg.eps)
+    v2 = F.linear(txt, W("attn2.to_v.weight"), W("attn2.to_v.bias"))
+    ki = F.rms_norm(F.linear(img, W("attn2.add_k_proj.weight"), W("attn2.add_k_proj.bias")), (d,),
+                    W("attn2.norm_added_k.weight"), cfg.eps)
+    vi = F.linear(img, W("attn2.add_v_proj.weight"), W("attn2.add_v_proj.bias"))
+    a2 = (F.scaled_dot_product_attention(heads(q2), heads(k2), heads(v2))
+          + F.scaled_dot_product_attention(heads(q2), heads(ki), heads(vi))).transpose(1, 2).flatten(2)
+    x2 = x1 + F.linear(a2, W("attn2.to_out.weight"), W("attn2.to_out.bias"))
+    mod = (W("scale_shift_table") + T(tproj)).chunk(6, dim=1)
+    y3 = F.layer_norm(x2, (d,), eps=cfg.eps) * (1 + mod[4]) + mod[3]
+    h = F.gelu(F.linear(y3, W("ffn.proj_in.weight"), W("ffn.proj_in.bias")), approximate="tanh")
+    ref = x2 + F.linear(h, W("ffn.proj_out.weight"), W("ffn.proj_out.bias")) * mod[5]
+    assert np.abs(got - ref.numpy()).max() < 1e-11
+
+
+def test_image_branch_constant_keys_add_mean_of_image_values():
+    cfg = _i2v_cfg()
+    w, x, _, tproj, ang = _block_setup(cfg)
+    d = cfg.dim
+    w.set("blocks.0.attn2.add_k_proj.weight", np.zeros((d, d)))   # every image key equal
+    rng = np.random.default_rng(29)
+    ctx = rng.standard_normal((1, cfg.image_len + cfg.text_len, d))
+    y2 = rng.standard_normal((1, cfg.tokens, d))
+    with_img = O._cross_attention(y2, ctx, w, "blocks.0.", cfg.num_heads, cfg.eps, cfg.image_len, 1)
+    text_only = O._cross_attention(y2, ctx[:, cfg.image_len:], w, "blocks.0.", cfg.num_heads, cfg.eps, 0, 1)
+    vi = O.linear(ctx[:, :cfg.image_len], w.f64("blocks.0.attn2.add_v_proj.weight"),
+                  w.f64("blocks.0.attn2.add_v_proj.bias"))
+    assert np.allclose(with_img - text_only, vi.mean(axis=1, keepdims=True), rtol=0, atol=1e-12)
+
+
+def test_image_tokens_permutation_invariance():
+    cfg = _i2v_cfg()
+    w, x, _, tproj, ang = _block_setup(cfg)
+    rng = np.random.default_rng(30)
+    ctx = rng.standard_normal((1, cfg.image_len + cfg.text_len, cfg.dim))
+    perm = np.concatenate([rng.permutation(cfg.image_len), cfg.image_len + np.arange(cfg.text_len)])
+    y1 = O.block_forward(x, ctx, tproj, ang, w, "blocks.0.", cfg.num_heads, cfg.eps, n_img=cfg.image_len)
+    y2 = O.block_forward(x, ctx[:, perm], tproj, ang, w, "blocks.0.", cfg.num_heads, cfg.eps, n_img=cfg.image_len)
+    assert np.allclose(y1, y2, rtol=0, atol=1e-12)
+    # moving an image token into the text part changes the result (the split is by position)
+    y3 = O.block_forward(x, ctx, tproj, ang, w, "blocks.0.", cfg.num_heads, cfg.eps, n_img=cfg.image_len - 1)
+    assert np.abs(y3 - y1).max() > 1e-6
+
+
+# ------------------------------------------------------------------------------------------------
+# Row-restricted block and forward (the evaluation of the largest workload on sampled tokens)
+# ------------------------------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("per_token", [False, True])
+def test_block_rows_equal_full_block(per_token):
+    cfg = tiny_cfg(batch=2)
+    w, x, ctx, tproj, ang = _block_setup(cfg)
+    if per_token:
+        tproj = np.random.default_rng(31).standard_normal((2, cfg.tokens, 6, cfg.dim)) * 0.3
+    full = _run_block(cfg, w, x, ctx, tproj, ang)
+    for rows in (np.array([0, 7, 3, cfg.tokens - 1]), np.arange(cfg.tokens)):
+        got = O.block_forward_rows(x, ctx, tproj, ang, w, "blocks.0.", cfg.num_heads, rows, cfg.eps)
+        assert np.abs(got - full[:, rows]).max() <= 1e-12 * np.abs(full).max()
+
+
+def test_forward_rows_equal_full_forward():
+    cfg = tiny_cfg(batch=1)
+    w = Weights(cfg)
+    lat, t, txt = draw_inputs(cfg)
+    out = O.forward(cfg, w, lat.f64(), t.f64(), txt.f64())
+    rows = np.array([1, 9, 12, cfg.tokens - 1])
+    z = O.forward_rows(cfg, w, lat.f64(), t.f64(), txt.f64(), rows)
+    hp, wp = cfg.post_h, cfg.post_w
+    c_out = cfg.out_channels
+    for r, n in enumerate(rows):
+        f, hh, ww = n // (hp * wp), (n // wp) % hp, n % wp
+        for i in range(2):
+            for j in range(2):
+                ref = out[0, :, f, 2 * hh + i, 2 * ww + j]
+                got = z[0, r, (2 * i + j) * c_out:(2 * i + j + 1) * c_out]
+                assert np.abs(got - ref).max() <= 1e-12 * np.abs(out).max()

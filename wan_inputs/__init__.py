@@ -5,6 +5,7 @@ from .generate import (  # noqa: F401
     Tensor,
     Weights,
     bf16_bits_to_f32,
+    draw_image,
     draw_inputs,
     draw_latent,
     draw_normal,

@@ -27,6 +27,8 @@ class WanConfig:
     text_len: int        # Lt
     dtype: str           # "f32" or "bf16": storage type of latent / text / Linear weights
     per_token_t: bool = False
+    image_len: int = 0   # CLIP image tokens of the I2V branch (0: no image branch)
+    image_dim: int = 1280
     head_dim: int = 128
     text_dim: int = 4096
     freq_dim: int = 256
@@ -80,6 +82,10 @@ class WanConfig:
         return (self.batch, self.text_len, self.text_dim)
 
     @property
+    def image_shape(self) -> tuple:
+        return (self.batch, self.image_len, self.image_dim)
+
+    @property
     def t_shape(self) -> tuple:
         return (self.batch, self.tokens) if self.per_token_t else (self.batch,)
 
@@ -125,7 +131,8 @@ def weight_spec(cfg: WanConfig):
     distribution only.  The inventory follows the module names the diffusers notes print
     (patch_embedding, condition_embedder / time_embedder, blocks[k].scale_shift_table, attn1, attn2,
     norm2, ffn, scale_shift_table, proj_out); the Linear structure inside the time and text embedders
-    is the reading stated with the oracle.
+    is the reading stated with the oracle.  With image tokens (the I2V branch) the image MLP and, per
+    block, the image keys' and values' projections and key norm gain are added.
     """
     D, Fd = cfg.dim, cfg.ffn_dim
     spec = []
@@ -141,6 +148,9 @@ def weight_spec(cfg: WanConfig):
     lin("time_proj", 6 * D, D)
     lin("text_embedder.linear_1", D, cfg.text_dim)
     lin("text_embedder.linear_2", D, D)
+    if cfg.image_len:
+        lin("image_embedder.linear_1", D, cfg.image_dim)
+        lin("image_embedder.linear_2", D, D)
     for k in range(cfg.num_layers):
         p = f"blocks.{k}."
         spec.append((p + "scale_shift_table", (1, 6, D), "table"))
@@ -149,6 +159,10 @@ def weight_spec(cfg: WanConfig):
                 lin(p + f"{a}.{proj}", D, D)
             spec.append((p + f"{a}.norm_q.weight", (D,), "gamma"))
             spec.append((p + f"{a}.norm_k.weight", (D,), "gamma"))
+        if cfg.image_len:
+            lin(p + "attn2.add_k_proj", D, D)
+            lin(p + "attn2.add_v_proj", D, D)
+            spec.append((p + "attn2.norm_added_k.weight", (D,), "gamma"))
         spec.append((p + "norm2.weight", (D,), "gamma"))
         spec.append((p + "norm2.bias", (D,), "beta"))
         lin(p + "ffn.proj_in", Fd, D)

@@ -11,6 +11,7 @@ Distributions (the reading stated for the synthetic workload):
   norm gains                        U[0.5, 1.5]       (a gain-indexing bug is visible, unlike gain == 1)
   norm biases                       N(0, 0.02)
   latent noise, text embedding      N(0, 1)           (the notes feed torch.randn text embeddings)
+  CLIP image tokens (I2V branch)    N(0, 1)
   timestep                          500 per sample, or U[0, 1000) per token
 
 This module holds no model arithmetic: only random draws, rounding to the storage type, and the
@@ -148,6 +149,14 @@ def draw_text(cfg: WanConfig, seed: int = ROOT_SEED) -> Tensor:
     rng = _rng(cfg.cfg_id, "input.text", seed)
     v = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
     return _store("input.text", cfg.dtype, shape, v)
+
+
+def draw_image(cfg: WanConfig, seed: int = ROOT_SEED) -> Tensor:
+    """CLIP image tokens [B, image_len, image_dim] N(0, 1), stand-ins for the encoder's features."""
+    shape = cfg.image_shape
+    rng = _rng(cfg.cfg_id, "input.image", seed)
+    v = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+    return _store("input.image", cfg.dtype, shape, v)
 
 
 def draw_timestep(cfg: WanConfig, seed: int = ROOT_SEED) -> Tensor:
