@@ -80,7 +80,7 @@ def time_self_attention(B, cfg, reps, stream):
     ldv = (L + 63) // 64 * 64
     vt = Bd.op_transpose_v(qkv, 2 * D, B, L, nh, ldv, stream=stream)
     out = torch.empty((B * L, D), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(Bd.attention_workspace_bytes() // 4, dtype=torch.float32, device="cuda")
+    ws = torch.empty((Bd.attention_workspace_bytes(B, L, nh) + 3) // 4, dtype=torch.float32, device="cuda")
     for _ in range(2):
         Bd.op_attention_ws(qkv, qkv[:, D:], vt, out, B, L, L, nh, workspace=ws, stream=stream)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -95,47 +95,44 @@ def time_self_attention(B, cfg, reps, stream):
 
 
 def cpu_baseline(cfg, budget_s: float):
-    """fp64 oracle on a bounded sample: one transformer block for one batch element of the workload,
-    with the self-attention restricted to a sample of query rows; scaled to one full step."""
+    """fp64 oracle on a bounded sample of the workload's own seeded inputs, scaled to one full step.
+
+    The embeddings (patch, time, text) run once in full.  A block costs a + b*L: the keys and values of
+    all L tokens (a) plus the per-token rest - the query, its self-attention over all keys, cross-
+    attention, FFN (b per token).  oracle.block_forward_rows on R1 and R2 token rows of block 0 (batch
+    element 0) gives a and b; the step is embeddings + batch * blocks * (a + b*L).  Each term is counted
+    once."""
     import numpy as np
 
     from oracle import wan_oracle as O
-    from wan_inputs import Weights
+    from wan_inputs import Weights, draw_inputs
 
     threads = len(os.sched_getaffinity(0))
     one = cfg.replace(batch=1, num_layers=1)
     w = Weights(one)
-    rng = np.random.default_rng(0)
-    L, D, nh = one.tokens, one.dim, one.num_heads
-    x = rng.standard_normal((1, L, D))
-    ctx = rng.standard_normal((1, one.text_len, D))
-    tproj = rng.standard_normal((1, 6, D)) * 0.1
-    ang = O.rope_angles(one.post_f, one.post_h, one.post_w)
+    lat, t, txt = draw_inputs(one)
     for n in w.names():
         w.f64(n)
-    p = "blocks.0."
-    # Untimed: q/k/v of all L tokens, so the self-attention sample sees every key.
-    y = O.layer_norm(x, one.eps)
-    q = O.rms_norm(O.linear(y, w.f64(p + "attn1.to_q.weight"), w.f64(p + "attn1.to_q.bias")), one.eps)
-    k = O.rms_norm(O.linear(y, w.f64(p + "attn1.to_k.weight"), w.f64(p + "attn1.to_k.bias")), one.eps)
-    v = O.linear(y, w.f64(p + "attn1.to_v.weight"), w.f64(p + "attn1.to_v.bias"))
-    nq = 2048
-    qh = O.apply_rope(q[0].reshape(L, nh, 128), ang)[:nq]
-    kh = O.apply_rope(k[0].reshape(L, nh, 128), ang)
-    vh = v[0].reshape(L, nh, 128)
-    del y, q, k, v
-    # Timed sample: self-attention of nq query rows per head against all L keys, plus one whole block
-    # (projections, cross-attention, FFN, norms) on nq tokens; both scale linearly to L tokens.
-    t1 = time.perf_counter()
-    O.attention(qh, kh, vh, workers=threads)
-    t_attn = time.perf_counter() - t1
-    t2 = time.perf_counter()
-    O.block_forward(x[:, :nq], ctx, tproj, ang[:nq], w, p, nh, one.eps)
-    t_rest = time.perf_counter() - t2
-    est_block = (t_attn + t_rest) * (L / nq)
-    est_step = est_block * cfg.batch * cfg.num_layers
-    sample_s = t_attn + t_rest
-    return est_step, sample_s, threads, nq
+    t0 = time.perf_counter()
+    x = O.patch_embed(lat.f64(), w.f64("patch_embedding.weight"), w.f64("patch_embedding.bias"))
+    temb, tproj = O.time_embed(t.f64(), w, one.freq_dim)
+    ctx = O.text_embed(txt.f64(), w)
+    ang = O.rope_angles(one.post_f, one.post_h, one.post_w, one.head_dim, one.rope_dims, one.rope_theta)
+    t_embed = time.perf_counter() - t0
+    L = one.tokens
+    r1, r2 = min(256, L), min(1024, L)
+    rng = np.random.default_rng(0)
+    times = []
+    for r in (r1, r2):
+        rows = np.sort(rng.choice(L, r, replace=False))
+        t1 = time.perf_counter()
+        O.block_forward_rows(x, ctx, tproj, ang, w, "blocks.0.", one.num_heads, rows, one.eps, workers=threads)
+        times.append(time.perf_counter() - t1)
+    b = max((times[1] - times[0]) / max(r2 - r1, 1), 0.0)
+    a = max(times[0] - b * r1, 0.0)
+    est_step = t_embed * cfg.batch + cfg.batch * cfg.num_layers * (a + b * L)
+    sample_s = t_embed + sum(times)
+    return est_step, sample_s, threads, (r1, r2, a, b, t_embed)
 
 
 def probe(cfg):
@@ -363,14 +360,15 @@ def main():
                      "traffic": traffic_for("k_attn.hip")},
     }
     if not args.no_cpu_baseline:
-        est_step, sample_s, threads, nq = cpu_baseline(cfg, args.cpu_budget)
+        est_step, sample_s, threads, (r1, r2, a, b, t_embed) = cpu_baseline(cfg, args.cpu_budget)
         res["cpu_baseline"] = {
             "value": round(fl["total"] / est_step / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "ms_per_step": round(est_step * 1e3, 1),
-            "sample": f"fp64 numpy oracle: one block for one batch element ({cfg.tokens} tokens) with self-attention "
-                      f"on {nq} query rows per head against all keys plus the rest of the block on {nq} tokens, "
-                      f"{sample_s:.1f}s measured, scaled x{cfg.tokens}/{nq} (tokens) x{cfg.batch} (batch) "
-                      f"x{cfg.num_layers} (blocks)",
+            "sample": f"fp64 numpy oracle on the workload's seeded inputs, batch element 0: the embeddings in full "
+                      f"({t_embed:.2f}s), then block 0 on {r1} and on {r2} token rows (keys/values of all "
+                      f"{cfg.tokens} tokens each time); a block = {a:.2f}s + {b * 1e3:.3f}ms per token, so the step "
+                      f"= {cfg.batch} x embeddings + {cfg.batch} x {cfg.num_layers} blocks x ({a:.2f}s + "
+                      f"{cfg.tokens} tokens x {b * 1e3:.3f}ms); {sample_s:.1f}s measured",
         }
     print(json.dumps(res), flush=True)
 

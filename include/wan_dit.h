@@ -68,6 +68,10 @@ typedef struct {
  *   blocks.k.ffn.proj_in.weight [Fd, D] .bias [Fd]   blocks.k.ffn.proj_out.weight [D, Fd] .bias [D]
  *   scale_shift_table [1, 2, D]
  *   proj_out.weight [4*C_out, D]  proj_out.bias [4*C_out]
+ * and, with max_image_len > 0 (the I2V image branch):
+ *   image_embedder.linear_1.weight [D, image_dim] .bias [D]   image_embedder.linear_2.weight [D, D] .bias [D]
+ *   blocks.k.attn2.add_k_proj.weight [D, D] .bias [D]   blocks.k.attn2.add_v_proj.weight [D, D] .bias [D]
+ *   blocks.k.attn2.norm_added_k.weight [D]
  * Linear weights are nn.Linear layout [out, in].  Each may be WAN_F32 or WAN_BF16.
  */
 typedef struct {
@@ -97,6 +101,10 @@ typedef struct {
   int64_t max_batch;      /* workspace bounds checked by forward */
   int64_t max_tokens;     /* L per sample */
   int64_t max_text_len;   /* Lt */
+  int64_t max_image_len;  /* CLIP image tokens of the I2V branch (Wan2.1 walk-through page, section 4: 257
+                             tokens); 0 = no image branch (no image weights expected) */
+  int32_t image_dim;      /* width of the image tokens (1280 on that page); multiple of 8 */
+  int32_t reserved1;
 } wan_dit_config;
 
 typedef struct wan_dit wan_dit;
@@ -119,6 +127,35 @@ wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight* weights, 
  * Allocates nothing; enqueues on hip_stream and returns without synchronising. */
 wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
                            const wan_tensor* text_emb, wan_tensor* out, void* hip_stream);
+
+/* The forward with CLIP image tokens (the I2V branch; Wan2.1 walk-through page, section 4: 257 image
+ * tokens of width 1280 projected by an MLP to the model width and attended by a cross-attention of their
+ * own; the WanPipeline notes' forward concatenates them in front of the text context).  Per block the
+ * cross-attention output is softmax(q k_txt^T) v_txt + softmax(q k_img^T) v_img, with the image keys and
+ * values from attn2.add_k_proj / add_v_proj (keys RMS-normalised with attn2.norm_added_k), before the
+ * shared attn2.to_out projection.
+ *   image_emb [B, Li, image_dim] WAN_F32 or WAN_BF16, 1 <= Li <= max_image_len (needs max_image_len > 0)
+ * Everything else as wan_dit_forward. */
+wan_status wan_dit_forward_image(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
+                                 const wan_tensor* text_emb, const wan_tensor* image_emb, wan_tensor* out,
+                                 void* hip_stream);
+
+/* One guided flow-matching denoising step (Wan2.1 walk-through page, section 7: the guided velocity
+ * v_u + s (v_c - v_u) and the update x_next = x + (sigma_next - sigma) v; section 6.3 works such a step by
+ * hand).  Runs the forward as a batch of 2 on the same latent and timestep, with the conditional text
+ * first and the unconditional (negative) text second, and fuses the guidance and the Euler update into
+ * the unpatchify scatter:
+ *   x_next[0, c, f, y, x] = latent[0, c, f, y, x] + (sigma_next - sigma) (v_u + guidance_scale (v_c - v_u)),
+ *   c < out_channels (the first out_channels latent channels are the noisy sample; an I2V latent's
+ *   condition and mask channels follow them).
+ *   latent    [1, C_in, F, H_z, W_z] WAN_F32 or WAN_BF16     timestep [1] or [1, L] WAN_F32
+ *   text_pair [2, Lt, text_dim]                                image_emb NULL, or [1, Li, image_dim]
+ *   x_next    [1, C_out, F, H_z, W_z] with the latent's dtype, not aliasing the latent
+ * sigma, sigma_next and the timestep are the caller's schedule (the pages leave the shifted schedule
+ * open).  Needs max_batch >= 2.  Allocates nothing; asynchronous on hip_stream. */
+wan_status wan_dit_denoise_step(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
+                                const wan_tensor* text_pair, const wan_tensor* image_emb, float guidance_scale,
+                                float sigma, float sigma_next, wan_tensor* x_next, void* hip_stream);
 
 /* Release the handle's device buffers.  NULL is ignored. */
 void wan_dit_destroy(wan_dit* h);

@@ -32,6 +32,17 @@ wan_status wan_op_patchify(const void* latent, int32_t dtype, int64_t B, int64_t
 wan_status wan_op_unpatchify(const float* z, int64_t ldz, int64_t B, int64_t C, int64_t F, int64_t H_z, int64_t W_z,
                              void* out, int32_t out_dtype, void* stream);
 
+/* Guided Euler step fused into the unpatchify scatter (Wan2.1 walk-through page, section 7):
+ *   z fp32 [2L, ldz]: proj_out rows of the conditional batch element (rows [0, L)) then the
+ *   unconditional one (rows [L, 2L)), columns as for wan_op_unpatchify;
+ *   x [1, Cx, F, H_z, W_z] (dtype), Cx >= C: the model input, whose first C channels are the noisy sample;
+ *   x_next[0, c, f, 2h+i, 2w+j] = x[0, c, f, 2h+i, 2w+j] + (sigma_next - sigma) (v_u + s (v_c - v_u)),
+ *   v_c = z[n, (2i+j)*C + c], v_u = z[L + n, (2i+j)*C + c]; fp32 arithmetic, bf16 output rounds to nearest
+ *   even.  x_next must not alias x. */
+wan_status wan_op_cfg_euler(const float* z, int64_t ldz, int64_t C, int64_t F, int64_t H_z, int64_t W_z, const void* x,
+                            int64_t Cx, int32_t dtype, float guidance_scale, float sigma, float sigma_next, void* x_next,
+                            void* stream);
+
 /* GEMM with fused epilogue (every nn.Linear of the block; WanPipeline notes, WanTransformerBlock):
  *   acc[m, n] = sum_k x[m, k] * w[n, k] + bias[n]   x bf16 [M, ldx], w bf16 [N, ldw], bias fp32 [N]
  *   epilogue 0: out bf16 [m, n] = acc                 1: out bf16 = gelu_tanh(acc)
@@ -74,11 +85,13 @@ wan_status wan_op_rope_table(float* table, int32_t Fp, int32_t Hp, int32_t Wp, i
  *   for each row and each segment s in {a, b (if gamma_b != NULL)}: u = buf[row, off_s : off_s + D],
  *   u <- u / sqrt(mean(u^2) + eps) * gamma_s; then, if table != NULL, every 128-wide head has its
  *   channel pairs (2m, 2m+1) rotated by the angle of pair m for token n = row % L, decoded as
- *   (f, h, w) on the Fp x Hp x Wp grid.  D multiple of 512, at most 12288. */
+ *   (f, h, w) on the Fp x Hp x Wp grid.  Segment a is also multiplied by scale_a (1 for the plain norm;
+ *   the forward passes log2(e)/sqrt(128) for the queries, which its attention takes pre-multiplied), in
+ *   fp32 before the one bf16 rounding.  D multiple of 512, at most 12288. */
 wan_status wan_op_qk_norm_rope(void* buf, int64_t ld, int64_t rows, int64_t D, float eps, int64_t off_a,
                                const float* gamma_a, int64_t off_b, const float* gamma_b, const float* table,
                                int64_t L, int32_t Fp, int32_t Hp, int32_t Wp, int32_t dt, int32_t dh, int32_t dw,
-                               void* stream);
+                               float scale_a, void* stream);
 
 /* V re-layout for the attention kernel: src bf16 rows [B*L, ld], heads at columns
  * col_off + 128h .. +127 -> vt bf16 [B, nh, 128, ldv] with vt[b,h,d,l] = src[b*L + l, col_off + 128h + d]
@@ -91,22 +104,33 @@ wan_status wan_op_transpose_v(const void* src, int64_t ld, int64_t col_off, int6
  *   o[b*Lq + i, 128h + :] = sum_j softmax_j(q_i . k_j / sqrt(128)) v_j
  *   q = q[b*Lq + i, 128h + :] (row stride ldq), k_j = k[b*Lkv + j, 128h + :] (row stride ldk),
  *   v_j = vt[b, h, :, j] from wan_op_transpose_v (ldv >= Lkv rounded up to 64).
- * bf16 in / out, fp32 softmax. */
+ * bf16 in / out, fp32 softmax (online, with a running row max).  The queries are multiplied by
+ * log2(e)/sqrt(128) and rounded to bf16 as the kernel loads them, so the scores come out in base-2 units. */
 wan_status wan_op_attention(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt, int64_t ldv,
                             void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh, void* stream);
 
-/* The same attention with a caller-owned device workspace of wan_op_attention_workspace_bytes() bytes
- * (fp32-aligned; contents need no initialisation).  Workgroups are (batch, head, 256-query tile) units,
- * one per CU at a time; when the last round of units would occupy at most half of the CUs, its units are
- * split into key chunks of a multiple of 64 keys, each chunk writes its unnormalised output, row max
- * and row sum to the workspace, and a merge pass forms the softmax over all keys from them
- * (o = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c).  Results equal wan_op_attention's up to fp32
- * rounding.  The workspace is in use until the call's work on `stream` completes; calls that overlap
- * on one workspace race.  Errors: WAN_ERR_INVALID_ARG for a NULL or short workspace. */
+/* The same attention with a caller-owned device workspace of wan_op_attention_workspace_bytes(B, Lq, nh)
+ * bytes (16-byte aligned; contents need no initialisation), the way the forward runs it:
+ *   - The softmax first runs without any row max: probabilities are exp2 of the base-2 scores as they
+ *     are (the common offset cancels in the final division).  A 64-row block of a wave whose scores
+ *     leave the range where that is safe (a 16-key probability sum above 2^64, or a first 32-key block
+ *     whose max is below -60) drops its results, and a second pass with the exact running-max softmax
+ *     recomputes the (batch, head, 256-query) units marked so; it returns at once for every other unit.
+ *     The marks live in the workspace.
+ *   - Workgroups are (batch, head, 256-query tile) units, one per CU at a time; when the last round of
+ *     units would occupy at most half of the CUs, its units are split into key chunks of a multiple of
+ *     64 keys, each chunk writes its unnormalised output, exponent offset and row sum to the workspace,
+ *     and a merge pass forms the softmax over all keys from them
+ *     (o = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c).
+ * Results equal wan_op_attention's up to fp32 rounding.  The workspace is in use until the call's work on
+ * `stream` completes; calls that overlap on one workspace race.  Errors: WAN_ERR_INVALID_ARG for a NULL,
+ * misaligned or short workspace. */
 wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt, int64_t ldv,
                                void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh, void* workspace,
                                int64_t workspace_bytes, void* stream);
-int64_t wan_op_attention_workspace_bytes(void);
+/* Workspace bytes wan_op_attention_ws needs for B batches of Lq queries and nh heads (-1 for B or Lq
+ * negative or nh <= 0). */
+int64_t wan_op_attention_workspace_bytes(int64_t B, int64_t Lq, int32_t nh);
 
 /* Timestep embedding, fp32 throughout (WanAnimate page, configuration section: freq_dim 256, the
  * time embedder kept in fp32; WanPipeline notes: temb (B, D), timestep_proj (B, 6D)):

@@ -82,5 +82,5 @@ def test_validation_errors_without_gpu():
                            None) == 2                                                           # D % 256
     assert B._op_layernorm(1, 4, 1536, 1e-6, 0, 1, 1, 1, 0, 0, 0, 1, None, None, 2, 1, None, None, 0, 1,
                            None) == 1                                                           # gate missing
-    assert B._op_qk_norm_rope(1, 4608, 4, 1536, 1e-6, 0, 1, 1536, 1, 1, 10, 2, 2, 2, 44, 42, 42, None) == 2
+    assert B._op_qk_norm_rope(1, 4608, 4, 1536, 1e-6, 0, 1, 1536, 1, 1, 10, 2, 2, 2, 44, 42, 42, 1.0, None) == 2
     assert B._op_rope_table(1, 5, 8, 8, 44, 42, 40, 1e4, None) == 2                              # dims sum != 128

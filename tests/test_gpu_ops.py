@@ -13,6 +13,8 @@ import pytest
 from oracle import wan_oracle as O
 from wan_inputs import f32_to_bf16_bits
 
+QSCALE = 1.4426950408889634 / math.sqrt(128.0)   # log2(e) / sqrt(128): the scale the attention applies to q
+
 pytestmark = pytest.mark.gpu
 
 
@@ -224,10 +226,11 @@ def test_rope_table(G):
     assert np.abs(c_all - np.cos(ang)).max() < 1e-7 and np.abs(s_all - np.sin(ang)).max() < 1e-7
 
 
-@pytest.mark.parametrize("B,grid,D", [(1, (5, 8, 8), 1536), (2, (3, 6, 10), 3072), (1, (9, 22, 40), 5120),
-                                      (2, (21, 30, 52), 1536)])
-def test_qk_norm_rope(G, B, grid, D):
-    G.note(f"qk_norm_rope B={B} grid={grid} D={D}")
+@pytest.mark.parametrize("B,grid,D,scale_a", [(1, (5, 8, 8), 1536, 1.0), (2, (3, 6, 10), 3072, 1.0),
+                                              (1, (9, 22, 40), 5120, 1.0), (2, (21, 30, 52), 1536, 1.0),
+                                              (1, (5, 8, 8), 1536, QSCALE)])
+def test_qk_norm_rope(G, B, grid, D, scale_a):
+    G.note(f"qk_norm_rope B={B} grid={grid} D={D} scale_a={scale_a}")
     fp, hp, wp = grid
     L = fp * hp * wp
     rows = B * L
@@ -235,7 +238,7 @@ def test_qk_norm_rope(G, B, grid, D):
     gq_t, gk_t = G.draw_uniform(2, "gq", (D,), 0.5, 1.5), G.draw_uniform(2, "gk", (D,), 0.5, 1.5)
     v_before = G.bf16_bits(buf)[:, 2 * D:].copy()
     tab = G.B.op_rope_table(fp, hp, wp)
-    G.B.op_qk_norm_rope(buf, D, 1e-6, 0, G.to_device(gq_t), D, G.to_device(gk_t), tab, L, grid)
+    G.B.op_qk_norm_rope(buf, D, 1e-6, 0, G.to_device(gq_t), D, G.to_device(gk_t), tab, L, grid, scale_a=scale_a)
     G.sync()
     out_bits = G.bf16_bits(buf)
     assert np.array_equal(out_bits[:, 2 * D:], v_before)        # V untouched
@@ -243,7 +246,7 @@ def test_qk_norm_rope(G, B, grid, D):
     sel = np.arange(rows) if rows <= 20000 else np.unique(np.random.default_rng(1).integers(0, rows, 2000))
     ang = O.rope_angles(fp, hp, wp)
     for seg, g_t in ((0, gq_t), (1, gk_t)):
-        u = O.rms_norm(bh[sel, seg * D:(seg + 1) * D], 1e-6, g_t.f64())
+        u = O.rms_norm(bh[sel, seg * D:(seg + 1) * D], 1e-6, g_t.f64()) * (scale_a if seg == 0 else 1.0)
         # rotate row by row with the oracle (each row has its own token position)
         ref = np.empty_like(u)
         for i in range(len(sel)):
@@ -271,7 +274,15 @@ def test_rms_norm_single_segment(G):
 # ------------------------------------------------------------------------------------------------
 
 
-def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None, split=False):
+def _scaled_q_reference(q):
+    """q * log2(e)/sqrt(128) rounded to bf16 (nearest even), expressed back in natural units."""
+    from wan_inputs import bf16_bits_to_f32
+
+    qs = (q * QSCALE).astype(np.float32)
+    return bf16_bits_to_f32(f32_to_bf16_bits(qs)).astype(np.float64).reshape(q.shape) / QSCALE
+
+
+def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None, split=False, q_round=False):
     import torch
 
     D = 128 * nh
@@ -299,6 +310,8 @@ def _attn_case(G, B, Lq, Lkv, nh, fused, name, scale=1.0, rows=None, split=False
     for b in range(B):
         sel = np.arange(Lq) if rows is None else rows
         qb = qh[b * Lq:(b + 1) * Lq][sel].reshape(len(sel), nh, 128)
+        if q_round:
+            qb = _scaled_q_reference(qb)
         kb = kh[b * Lkv:(b + 1) * Lkv].reshape(Lkv, nh, 128)
         vb = vh[b * Lkv:(b + 1) * Lkv].reshape(Lkv, nh, 128)
         ref = O.attention(qb, kb, vb, workers=4).reshape(len(sel), D)
@@ -335,6 +348,18 @@ def test_attention_key_split_peaked(G):
     """Scores in the tens with chunked keys: the merge rescales chunks whose running maxima differ."""
     G.note("attention key split peaked")
     _attn_case(G, 1, 500, 500, 2, True, "kspeaked", scale=3.0, split=True)
+
+
+def test_attention_out_of_range_scores_redone_exactly(G):
+    """Scores of hundreds of base-2 units: the offset-free softmax leaves its range in every wave, so the
+    workspace path drops those results and its exact running-max pass recomputes them (with and without a
+    key-split last round); the plain entry point runs the exact kernel alone.  At such magnitudes the
+    near one-hot softmax follows the one bf16 rounding of q * log2(e)/sqrt(128) the entry points apply
+    (documented with them), so the reference takes the queries rounded that way."""
+    G.note("attention out-of-range scores")
+    for B, L, nh, split in ((1, 700, 3, True), (2, 2100, 4, True), (1, 500, 2, False)):
+        _attn_case(G, B, L, L, nh, True, f"oor{B}_{L}", scale=8.0, split=split, q_round=True)
+    _attn_case(G, 1, 300, 226, 2, False, "oorx", scale=8.0, split=True, q_round=True)
 
 
 def test_attention_peaked_scores(G):

@@ -44,7 +44,8 @@ class WanDitConfig(C.Structure):
                 ("patch_w", C.c_int32), ("rope_dim_t", C.c_int32), ("rope_dim_h", C.c_int32),
                 ("rope_dim_w", C.c_int32), ("per_token_timestep", C.c_int32), ("eps", C.c_float),
                 ("reserved0", C.c_float), ("rope_theta", C.c_double), ("max_batch", C.c_int64),
-                ("max_tokens", C.c_int64), ("max_text_len", C.c_int64)]
+                ("max_tokens", C.c_int64), ("max_text_len", C.c_int64), ("max_image_len", C.c_int64),
+                ("image_dim", C.c_int32), ("reserved1", C.c_int32)]
 
 
 _vp, _i64, _i32, _f32, _f64 = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_double
@@ -60,6 +61,10 @@ def _sig(name, args, res=C.c_int):
 _create = _sig("wan_dit_create", [C.POINTER(WanDitConfig), C.POINTER(WanWeight), C.c_size_t, _vp, C.POINTER(_vp)])
 _forward = _sig("wan_dit_forward", [_vp, C.POINTER(WanTensor), C.POINTER(WanTensor), C.POINTER(WanTensor),
                                     C.POINTER(WanTensor), _vp])
+_forward_image = _sig("wan_dit_forward_image", [_vp, C.POINTER(WanTensor), C.POINTER(WanTensor), C.POINTER(WanTensor),
+                                                C.POINTER(WanTensor), C.POINTER(WanTensor), _vp])
+_denoise_step = _sig("wan_dit_denoise_step", [_vp, C.POINTER(WanTensor), C.POINTER(WanTensor), C.POINTER(WanTensor),
+                                              C.POINTER(WanTensor), _f32, _f32, _f32, C.POINTER(WanTensor), _vp])
 _destroy = _sig("wan_dit_destroy", [_vp], None)
 _last_error = _sig("wan_dit_last_error", [], C.c_char_p)
 _device_bytes = _sig("wan_dit_device_bytes", [_vp], _i64)
@@ -74,18 +79,19 @@ _op_layernorm = _sig("wan_op_layernorm", [_vp, _i64, _i64, _f32, _i32, _vp, _vp,
 _op_rope_table_floats = _sig("wan_op_rope_table_floats", [_i32] * 6, _i64)
 _op_rope_table = _sig("wan_op_rope_table", [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _f64, _vp])
 _op_qk_norm_rope = _sig("wan_op_qk_norm_rope", [_vp, _i64, _i64, _i64, _f32, _i64, _vp, _i64, _vp, _vp, _i64, _i32,
-                                                _i32, _i32, _i32, _i32, _i32, _vp])
+                                                _i32, _i32, _i32, _i32, _i32, _f32, _vp])
+_op_cfg_euler = _sig("wan_op_cfg_euler", [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _i32, _f32, _f32, _f32, _vp, _vp])
 _op_transpose_v = _sig("wan_op_transpose_v", [_vp, _i64, _i64, _i64, _i64, _i32, _vp, _i64, _vp])
 _op_attention = _sig("wan_op_attention", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp])
 _op_attention_ws = _sig("wan_op_attention_ws", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp,
                                                 _i64, _vp])
-_op_attention_ws_bytes = _sig("wan_op_attention_workspace_bytes", [], C.c_int64)
+_op_attention_ws_bytes = _sig("wan_op_attention_workspace_bytes", [_i64, _i64, _i32], C.c_int64)
 _op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
 _probe_mfma = _sig("wan_probe_mfma", [_vp, _i32, _i64, _i32, _vp])
 
-EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
+EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_forward_image", "wan_dit_denoise_step", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
             "wan_dit_time_attention", "wan_dit_attention_time",
-            "wan_op_patchify", "wan_op_unpatchify", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
+            "wan_op_patchify", "wan_op_unpatchify", "wan_op_cfg_euler", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
             "wan_op_attention_ws", "wan_op_attention_workspace_bytes",
             "wan_op_time_embed", "wan_probe_mfma"]
@@ -144,6 +150,8 @@ def make_config(cfg, max_batch=None, max_tokens=None, max_text_len=None, num_lay
     c.max_batch = max_batch or cfg.batch
     c.max_tokens = max_tokens or cfg.tokens
     c.max_text_len = max_text_len or cfg.text_len
+    c.max_image_len = getattr(cfg, "image_len", 0)
+    c.image_dim = getattr(cfg, "image_dim", 1280)
     return c
 
 
@@ -182,6 +190,29 @@ class WanDiT:
             out = torch.empty((b, self.config.out_channels, f, hz, wz), dtype=latent.dtype, device=latent.device)
         lt, tt, xt, ot = (as_wan_tensor(latent), as_wan_tensor(timestep), as_wan_tensor(text), as_wan_tensor(out))
         _check(_forward(self._h, C.byref(lt), C.byref(tt), C.byref(xt), C.byref(ot), _stream(stream)))
+        return out
+
+    def forward_image(self, latent: torch.Tensor, timestep: torch.Tensor, text: torch.Tensor, image: torch.Tensor,
+                      out: torch.Tensor = None, stream=None) -> torch.Tensor:
+        if out is None:
+            b, _, f, hz, wz = latent.shape
+            out = torch.empty((b, self.config.out_channels, f, hz, wz), dtype=latent.dtype, device=latent.device)
+        lt, tt, xt, it, ot = (as_wan_tensor(latent), as_wan_tensor(timestep), as_wan_tensor(text), as_wan_tensor(image),
+                              as_wan_tensor(out))
+        _check(_forward_image(self._h, C.byref(lt), C.byref(tt), C.byref(xt), C.byref(it), C.byref(ot), _stream(stream)))
+        return out
+
+    def denoise_step(self, latent: torch.Tensor, timestep: torch.Tensor, text_pair: torch.Tensor, guidance_scale: float,
+                     sigma: float, sigma_next: float, image: torch.Tensor = None, out: torch.Tensor = None,
+                     stream=None) -> torch.Tensor:
+        """x_next [1, C_out, F, H, W] = x + (sigma_next - sigma) (v_u + s (v_c - v_u)) (wan_dit_denoise_step)."""
+        if out is None:
+            _, _, f, hz, wz = latent.shape
+            out = torch.empty((1, self.config.out_channels, f, hz, wz), dtype=latent.dtype, device=latent.device)
+        lt, tt, xt, ot = as_wan_tensor(latent), as_wan_tensor(timestep), as_wan_tensor(text_pair), as_wan_tensor(out)
+        it = as_wan_tensor(image) if image is not None else None
+        _check(_denoise_step(self._h, C.byref(lt), C.byref(tt), C.byref(xt), C.byref(it) if it is not None else None,
+                             guidance_scale, sigma, sigma_next, C.byref(ot), _stream(stream)))
         return out
 
     def time_attention(self, max_launches: int):
@@ -257,11 +288,21 @@ def op_rope_table(fp: int, hp: int, wp: int, dims=(44, 42, 42), theta: float = 1
 
 def op_qk_norm_rope(buf: torch.Tensor, d: int, eps: float, off_a: int, gamma_a: torch.Tensor, off_b: int = 0,
                     gamma_b: torch.Tensor = None, table: torch.Tensor = None, L: int = 1, grid=(1, 1, 1),
-                    dims=(44, 42, 42), stream=None):
+                    dims=(44, 42, 42), scale_a: float = 1.0, stream=None):
     rows = buf.shape[0]
     _check(_op_qk_norm_rope(buf.data_ptr(), buf.stride(0), rows, d, eps, off_a, gamma_a.data_ptr(), off_b,
-                            _ptr(gamma_b), _ptr(table), L, *grid, *dims, _stream(stream)))
+                            _ptr(gamma_b), _ptr(table), L, *grid, *dims, scale_a, _stream(stream)))
     return buf
+
+
+def op_cfg_euler(z: torch.Tensor, c: int, x: torch.Tensor, guidance_scale: float, sigma: float, sigma_next: float,
+                 stream=None) -> torch.Tensor:
+    """z fp32 [2L, >= 4c] (conditional rows first), x [1, Cx, F, H, W] -> x_next [1, c, F, H, W] (x's dtype)."""
+    _, cx, f, hz, wz = x.shape
+    out = torch.empty((1, c, f, hz, wz), dtype=x.dtype, device=x.device)
+    _check(_op_cfg_euler(z.data_ptr(), z.stride(0), c, f, hz, wz, x.data_ptr(), cx, _dtype_code(x), guidance_scale, sigma,
+                         sigma_next, out.data_ptr(), _stream(stream)))
+    return out
 
 
 def op_transpose_v(src: torch.Tensor, col_off: int, b: int, L: int, nh: int, ldv: int, stream=None):
@@ -278,16 +319,17 @@ def op_attention(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.
     return out
 
 
-def attention_workspace_bytes() -> int:
-    return int(_op_attention_ws_bytes())
+def attention_workspace_bytes(b: int, lq: int, nh: int) -> int:
+    return int(_op_attention_ws_bytes(b, lq, nh))
 
 
 def op_attention_ws(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Tensor, b: int, lq: int, lkv: int,
                     nh: int, workspace: torch.Tensor = None, stream=None):
-    """op_attention with a device workspace (allocated here when not given): the last round of
-    workgroups may be split over key chunks and merged."""
+    """op_attention with a device workspace (allocated here when not given), as the forward runs it:
+    offset-free softmax with an exact redo pass, and the last round of workgroups possibly split over
+    key chunks and merged."""
     if workspace is None:
-        workspace = torch.empty(attention_workspace_bytes() // 4, dtype=torch.float32, device=q.device)
+        workspace = torch.empty((attention_workspace_bytes(b, lq, nh) + 3) // 4, dtype=torch.float32, device=q.device)
     _check(_op_attention_ws(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(), vt.shape[3],
                             out.data_ptr(), out.stride(0), b, lq, lkv, nh, workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(stream)))

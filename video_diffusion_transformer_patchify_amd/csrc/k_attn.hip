@@ -24,12 +24,15 @@
 //   * Keys are processed in 32-key sub-tiles j, software pipelined: the MFMAs of S(j+1) are issued
 //     together with the exp / row-sum / bf16 packing of S(j), and the PV MFMAs of sub-tile j together
 //     with the row max of S(j+1), so matrix and vector work of one wave overlap.
-//   * Softmax in base 2 with the 1/sqrt(128) scale folded into one FMA per score.  The running max is
-//     only raised when a sub-tile's max exceeds it by more than 8 (log2 units): until then the stale
-//     max is kept (probabilities up to 2^8, exact after the final division because numerator and
-//     denominator share it) and the O rescale is skipped.
-//   * Row max is shared between the two lane halves with one cross-lane exchange per sub-tile; row
-//     sums stay per lane half and are combined once at the end.
+//   * Softmax in base 2: Q enters the score MFMAs multiplied by log2(e)/sqrt(128), so S is already
+//     in log2 units and a probability is one exp2 of an accumulator value, with no offset: the row's
+//     scores are not reduced to a running max at all while they stay in a safe range (any common
+//     offset of numerator and denominator cancels in the final division).  Each sub-tile's per-lane
+//     probability sum is checked against 2^64, and the first sub-tile's row max against -60; a wave
+//     whose rows leave that range (scores beyond ~60 log2 units) switches, from there on, to the exact online
+//     softmax with a running max m, raised only when a sub-tile's max passes it by more than 8 (the
+//     stale max keeps probabilities below 2^8), rescaling O and l when it is.
+//   * Row sums stay per lane half and are combined once at the end.
 //   * Only the last sub-tile can be partial; its scores are masked in a peeled copy of the loop body.
 #include <type_traits>
 
@@ -46,7 +49,9 @@ constexpr int QB = 4 * QWAVE;       // queries per workgroup
 constexpr int K_TILE_BYTES = KT * 256;     // 64 rows of 128 bf16
 constexpr int V_TILE_BYTES = 128 * KT * 2; // 128 rows of 64 bf16
 constexpr int TILE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
-constexpr float RESCALE_LOG2 = 8.0f;
+constexpr float SUM_LIMIT = 18446744073709551616.0f;   // 2^64: largest per-lane sub-tile sum, offset-free
+constexpr float MAX_FLOOR = -60.0f;                    // smallest first-sub-tile row max, offset-free
+constexpr float RESCALE_LOG2 = 8.0f;                   // exact path: margin before the running max is raised
 constexpr int64_t ATTN_SPLIT_MAX = 256;   // workgroups of a key-split launch (workspace size)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -60,13 +65,16 @@ struct AttnArgs {
   int nh, B;
   int q_tiles;
   float scale_log2;   // log2(e) / sqrt(128)
+  float q_mul;        // factor applied to Q as it is loaded (1 when the caller stored Q pre-multiplied)
   int units;          // workgroups of the regular launch: units 0 .. units-1, unit = (b, h, query tile)
   // key-split launch: workgroup w works on unit units_base + w / split over keys
   // [chunk (w % split), chunk (w % split + 1)) and writes unnormalised partial results
   int split, units_base;
   int64_t chunk;
   float* part_o;      // [w][256 queries][128]: sum over the chunk's keys of p * v (p relative to m)
-  float* part_ml;     // [w][256 queries][2]: running max m (raw score units) and row sum l
+  float* part_ml;     // [w][256 queries][2]: exponent offset m (log2 units) and row sum l
+  unsigned* flags;    // per workgroup, 4 wave flags: results dropped, recompute exactly (see k_flash_attn)
+  int accumulate;     // 1: o += this attention's output (o holds another key set's normalised output)
 };
 
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
@@ -83,8 +91,9 @@ __device__ __forceinline__ int v_swz(int r) { return ((r >> 1) ^ (r << 2)) & 7; 
 
 struct AttnState {
   f32x16 o[2][4];
-  float m_run[2], l_run[2];
-  float mc[2];   // -m_run * c, the exponent offset of the probabilities
+  float l_run[2];   // this lane half's sum of the row's probabilities
+  float m[2];       // exponent offset of the probabilities (log2 units): 0 offset-free, else the running max
+  bool bad;         // offset-free kernel, wave-uniform: a row left the safe range (the unit is redone exactly)
 };
 
 // S^T for sub-tile `sub` (0 or 1) of an LDS tile, both query blocks; each K fragment read once.
@@ -114,37 +123,62 @@ __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int g, int key_lim) 
     }
 }
 
-// Row max of a sub-tile's scores for both query blocks (both lane halves agree).
-__device__ __forceinline__ void row_max(f32x16 (&s)[2], float (&mx)[2]) {
+// One copy of the scores out of the accumulator registers into the registers the softmax reads (the
+// loop then carries them there: the prologue's and the loop's copies meet in the same registers).
+__device__ __forceinline__ void to_vgprs(const f32x16 (&src)[2], f32x16 (&dst)[2]) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = s[qb][r];
-      asm volatile("" : "+v"(x));   // one copy out of the accumulator registers, reused by probs()
-      s[qb][r] = x;
+      float x = src[qb][r];
+      asm volatile("" : "+v"(x));
+      dst[qb][r] = x;
     }
+}
+
+// Row max of one query block's sub-tile scores (both lane halves agree).
+__device__ __forceinline__ float row_max(const f32x16& s) {
+  float m = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) m = fmaxf(m, s[r]);
+  // lanes 0-31 and 32-63 hold the two key halves of the same queries: swap halves and combine
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// P = exp2(s - m) as bf16 B-operand fragments (two 16-key steps per query block) and this lane's sums.
+template <bool OFFSET>
+__device__ __forceinline__ void probs(const f32x16 (&s)[2], const float (&m)[2], u32x4 (&pf)[2][2], float (&ls)[2]) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float m = fmaxf(s[qb][0], s[qb][1]);
+    float sum;
 #pragma unroll
-    for (int r = 2; r < 16; ++r) m = fmaxf(m, s[qb][r]);
-    // lanes 0-31 and 32-63 hold the two key halves of the same queries: swap halves and combine
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    mx[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    for (int hh = 0; hh < 2; ++hh) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(OFFSET ? s[qb][8 * hh + e] - m[qb] : s[qb][8 * hh + e]);
+        sum = (hh == 0 && e == 0) ? p[e] : sum + p[e];
+      }
+      u32x4 w;
+      w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]);
+      w.z = pack_bf16x2(p[4], p[5]); w.w = pack_bf16x2(p[6], p[7]);
+      pf[qb][hh] = w;
+    }
+    ls[qb] = sum;
   }
 }
 
-// Raise the running max where a sub-tile's max passed it by more than the margin; rescale O and l.
-__device__ __forceinline__ void maybe_rescale(AttnState& st, const float (&mx)[2], float c, float grow_thr) {
+// Exact path: raise the running max where this sub-tile's max passed it by more than 8; rescale O, l.
+__device__ __forceinline__ void raise_max(AttnState& st, const f32x16 (&s)[2]) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const bool grow = mx[qb] > st.m_run[qb] + grow_thr;
+    const float mx = row_max(s[qb]);
+    const bool grow = mx > st.m[qb] + RESCALE_LOG2;
     if (__any(grow)) {
-      const float m_new = grow ? mx[qb] : st.m_run[qb];
-      const float alpha = __builtin_amdgcn_exp2f((st.m_run[qb] - m_new) * c);
-      st.m_run[qb] = m_new;
-      st.mc[qb] = -m_new * c;
+      const float m_new = grow ? mx : st.m[qb];
+      const float alpha = __builtin_amdgcn_exp2f(st.m[qb] - m_new);
+      st.m[qb] = m_new;
       st.l_run[qb] *= alpha;
       // one 16-register accumulator at a time: they live in AGPRs, each multiply needs VGPR temporaries
 #pragma unroll
@@ -156,27 +190,21 @@ __device__ __forceinline__ void maybe_rescale(AttnState& st, const float (&mx)[2
   }
 }
 
-// P = exp2(s c - m c) as bf16 B-operand fragments (two 16-key steps per query block); l += row sums.
-__device__ __forceinline__ void probs(AttnState& st, const f32x16 (&s)[2], u32x4 (&pf)[2][2], float c) {
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float mc = st.mc[qb];
-    float ls;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * hh + e], c, mc));
-        ls = (hh == 0 && e == 0) ? p[e] : ls + p[e];
-      }
-      u32x4 w;
-      w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]);
-      w.z = pack_bf16x2(p[4], p[5]); w.w = pack_bf16x2(p[6], p[7]);
-      pf[qb][hh] = w;
-    }
-    st.l_run[qb] += ls;
+// Probabilities of the current sub-tile into pf; l accumulates their sums.  EXACT: against the running
+// max.  Otherwise offset-free; a lane sum above SUM_LIMIT marks the wave bad (its results are dropped and
+// its unit is recomputed by the exact kernel).
+template <bool EXACT>
+__device__ __forceinline__ void softmax_step(AttnState& st, const f32x16 (&s)[2], u32x4 (&pf)[2][2]) {
+  float ls[2];
+  if constexpr (EXACT) {
+    raise_max(st, s);
+    probs<true>(s, st.m, pf, ls);
+  } else {
+    probs<false>(s, st.m, pf, ls);
+    st.bad |= __any(!(fmaxf(ls[0], ls[1]) <= SUM_LIMIT));   // branch-free: the loop stays one block
   }
+  st.l_run[0] += ls[0];
+  st.l_run[1] += ls[1];
 }
 
 // O^T += V^T P^T for sub-tile `sub` of an LDS tile: A = Vt rows d = 32 dt + l32, keys 32 sub + 16 jj + 8 g.
@@ -197,8 +225,13 @@ __device__ __forceinline__ void pv(AttnState& st, const u32x4 (&pf)[2][2], const
 
 // SELF selects the instantiation only (self- and cross-attention then show up as separate kernels in
 // a trace); the code path is the same.  PART: one key chunk of a unit, unnormalised output (see
-// AttnArgs); the last round of a launch that would leave most CUs idle is run this way.
-template <bool SELF, bool PART>
+// AttnArgs); the last round of a launch that would leave most CUs idle is run this way.  EXACT: the
+// online softmax with a running max.  The offset-free kernel (EXACT false) writes, per wave, whether
+// its rows stayed in range to a.flags[4 w + wave] (w = the workgroup's unit, or its split workgroup)
+// and drops the results of a wave that did not; the exact kernel launched after it with the same
+// grid recomputes exactly the workgroups with a flag set and returns at once for the others.  With
+// a.flags null the exact kernel computes every workgroup.
+template <bool SELF, bool PART, bool EXACT>
 __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NBUF][TILE_BYTES];
 
@@ -208,6 +241,13 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   // Workgroups of one (batch, head) are kept on one XCD so they share K/V in its L2.
   const int lid = PART ? a.units_base + (int)blockIdx.x / a.split : xcd_remap(blockIdx.x, a.units);
+  const int wg = PART ? (int)blockIdx.x : lid;   // index of this workgroup's redo flags
+  if constexpr (EXACT) {
+    if (a.flags != nullptr) {
+      const u32x4 f = *(const u32x4*)(a.flags + 4 * (int64_t)wg);
+      if ((f.x | f.y | f.z | f.w) == 0u) return;   // whole workgroup, before any barrier
+    }
+  }
   const int64_t k_lo = PART ? (int64_t)((int)blockIdx.x % a.split) * a.chunk : 0;
   // keys of this workgroup: [k_lo, k_lo + Lkv) of its (batch, head)
   const int64_t Lkv = PART ? (a.Lkv - k_lo < a.chunk ? a.Lkv - k_lo : a.chunk) : a.Lkv;
@@ -215,9 +255,10 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   const int bh = lid / a.q_tiles;
   const int h = bh % a.nh, b = bh / a.nh;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): query l32 of block qb, d = 16 s + 8 g .. +7
+  // ---- Q fragments (B operand of S^T = K Q^T): query l32 of block qb, d = 16 s + 8 g .. +7, times q_mul
   int64_t qi[2];
   u32x4 qf[2][8];
+  const bool scale_q = a.q_mul != 1.0f;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     qi[qb] = (int64_t)qt * QB + wave * QWAVE + qb * 32 + l32;
@@ -226,6 +267,10 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       u32x4 v = *(const u32x4*)(qp + 16 * s);
+      if (scale_q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(lo_bf16(v[e]) * a.q_mul, hi_bf16(v[e]) * a.q_mul);
+      }
       // MFMA source operands may come from AGPRs: Q lives there for the whole kernel, which leaves
       // the VGPRs to the score copies the softmax works on
       asm volatile("; q fragment %0" : "=a"(qf[qb][s]) : "0"(v));
@@ -286,12 +331,10 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.o[qb][i] = (f32x16){};
-    st.m_run[qb] = -INFINITY;
-    st.mc[qb] = INFINITY;
+    st.m[qb] = 0.f;
     st.l_run[qb] = 0.f;
   }
-  const float c = a.scale_log2;
-  const float grow_thr = RESCALE_LOG2 / c;   // raw-score margin before the max is raised
+  st.bad = false;
   const int last_lim = (int)(Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
 
   // vmcnt(n) for n in {0, 4, 8, 12, 16}, with or without lgkmcnt(0)
@@ -303,9 +346,8 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     else if (n >= 4) __builtin_amdgcn_s_waitcnt(L0 ? 0x0074 : 0x0F74);
     else __builtin_amdgcn_s_waitcnt(L0 ? 0x0070 : 0x0F70);
   };
-  // ---- prologue: K0, then [K1 V0] [K2 V1] [K3 V2] (the batches the barriers of tiles -3..-1 would
-  //      issue); tile 0 resident; scores and max of sub-tile 0
-  // batches of the barriers of tiles -4 and -2: [K0 K1 V0] [K2 K3 V1 V2]
+  // ---- prologue: batches of the barriers of tiles -4 and -2: [K0 K1 V0] [K2 K3 V1 V2]; tile 0
+  //      resident; scores of sub-tile 0 and the offsets from their row max
   issue(0, 0);
   if (1 < n_tiles) issue(1, 0);
   issue(0, 1);
@@ -319,19 +361,29 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   wait_vm(4 * ((2 < n_tiles) + (3 < n_tiles) + (1 < n_tiles) + (2 < n_tiles)), std::false_type{});
   block_sync();
   f32x16 s_cur[2], s_next[2];
-  float mx[2];
-  scores(s_cur, qf, lds[0], 0, l32, g);
-  if (n_sub == 1 && last_lim < KS) mask_scores(s_cur, g, last_lim);
-  row_max(s_cur, mx);
-  maybe_rescale(st, mx, c, grow_thr);
+  scores(s_next, qf, lds[0], 0, l32, g);
+  if (n_sub == 1 && last_lim < KS) mask_scores(s_next, g, last_lim);
+  to_vgprs(s_next, s_cur);
+  {
+    // the first sub-tile holds at least one key, so its row max is finite.  Exact: the running max
+    // starts there.  Offset-free: a row whose first sub-tile lies entirely below 2^-60 is out of range.
+    const float mx0 = row_max(s_cur[0]), mx1 = row_max(s_cur[1]);
+    if constexpr (EXACT) {
+      st.m[0] = mx0;
+      st.m[1] = mx1;
+    } else {
+      st.bad = __any(!(fminf(mx0, mx1) >= MAX_FLOOR));
+    }
+  }
 
-  // One pipelined step: S(j+1) with P(j); PV(j) with max(S(j+1)).  LAST: S(j+1) is the final sub-tile.
+  // One pipelined step j: head (barrier, loads, S(j+1)), the probabilities of sub-tile j, tail (PV(j)).
+  // LAST: S(j+1) is the final sub-tile.
   // The second half of an even tile t opens with the workgroup barrier that covers the next four
   // steps, which read tiles t, t+1 and t+2 only: own loads of tiles t+1 and t+2 landed (both went out
   // at the previous barrier or in the prologue: vmcnt(0)), then every wave's.  Every wave is also past
   // its last read of K(t) (first half of tile t) and of V(t-1) (second half of tile t-1), so the K
   // regions of tiles <= t and the V regions of tiles <= t-1 take K(t+4), K(t+5), V(t+3), V(t+4).
-  auto step = [&](int j, auto last_tag) {
+  auto head = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int t = j >> 1, half = j & 1;
     if (half && !(t & 1)) {
@@ -344,32 +396,46 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
       if (t + 3 < n_tiles) issue(t + 3, 1);
       if (t + 4 < n_tiles) issue(t + 4, 1);
     }
-    u32x4 pf[2][2];
     scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
-    probs(st, s_cur, pf, c);
     if constexpr (LAST) {
       if (last_lim < KS) mask_scores(s_next, g, last_lim);
     }
-    pv(st, pf, lds[t % NBUF] + K_TILE_BYTES, half, l32, g);
-    row_max(s_next, mx);
-    maybe_rescale(st, mx, c, grow_thr);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) s_cur[qb] = s_next[qb];
+  };
+  // PV of sub-tile j; the next sub-tile's scores become current
+  auto tail = [&](int j, const u32x4 (&pf)[2][2]) {
+    pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
+    to_vgprs(s_next, s_cur);
   };
   int j = 0;
-  for (; j + 2 < n_sub; ++j) step(j, std::false_type{});
+  for (; j + 2 < n_sub; ++j) {
+    u32x4 pf[2][2];
+    head(j, std::false_type{});
+    softmax_step<EXACT>(st, s_cur, pf);
+    tail(j, pf);
+  }
   if (j + 1 < n_sub) {
-    step(j, std::true_type{});
+    u32x4 pf[2][2];
+    head(j, std::true_type{});
+    softmax_step<EXACT>(st, s_cur, pf);
+    tail(j, pf);
     ++j;
   }
   // ---- last sub-tile j = n_sub - 1
   {
     u32x4 pf[2][2];
-    probs(st, s_cur, pf, c);
+    softmax_step<EXACT>(st, s_cur, pf);
     pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
   }
 
   // ---- normalise and store: o[qb][dt] element r holds d = 32 dt + 8 (r/4) + 4 g + r%4 of query qi[qb]
+  if constexpr (!EXACT) {
+    if (lane == 0) a.flags[4 * (int64_t)wg + wave] = st.bad ? 1u : 0u;
+    if (st.bad) return;
+  } else {
+    // redo pass: only the waves the offset-free kernel dropped store (the others' rows are in place,
+    // and with accumulate they must not be added twice)
+    if (a.flags != nullptr && a.flags[4 * (int64_t)wg + wave] == 0u) return;
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32, 64);
@@ -382,7 +448,7 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
         for (int rg = 0; rg < 4; ++rg)
           *(f32x4*)(po + 32 * dt + 8 * rg) = (f32x4){st.o[qb][dt][4 * rg], st.o[qb][dt][4 * rg + 1],
                                                      st.o[qb][dt][4 * rg + 2], st.o[qb][dt][4 * rg + 3]};
-      if (g == 0) *(f32x2*)(a.part_ml + ((int64_t)blockIdx.x * QB + qloc) * 2) = (f32x2){st.m_run[qb], l_tot};
+      if (g == 0) *(f32x2*)(a.part_ml + ((int64_t)blockIdx.x * QB + qloc) * 2) = (f32x2){st.m[qb], l_tot};
       continue;
     }
     const float inv = 1.0f / l_tot;
@@ -392,16 +458,22 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
+          float v[4] = {st.o[qb][dt][4 * rg] * inv, st.o[qb][dt][4 * rg + 1] * inv, st.o[qb][dt][4 * rg + 2] * inv,
+                        st.o[qb][dt][4 * rg + 3] * inv};
+          if (a.accumulate) {
+            const u32x2 prev = *(const u32x2*)(op + 32 * dt + 8 * rg);
+            v[0] += lo_bf16(prev.x); v[1] += hi_bf16(prev.x); v[2] += lo_bf16(prev.y); v[3] += hi_bf16(prev.y);
+          }
           u32x2 w;
-          w.x = pack_bf16x2(st.o[qb][dt][4 * rg] * inv, st.o[qb][dt][4 * rg + 1] * inv);
-          w.y = pack_bf16x2(st.o[qb][dt][4 * rg + 2] * inv, st.o[qb][dt][4 * rg + 3] * inv);
+          w.x = pack_bf16x2(v[0], v[1]);
+          w.y = pack_bf16x2(v[2], v[3]);
           *(u32x2*)(op + 32 * dt + 8 * rg) = w;
         }
     }
   }
 }
 
-// Merge of the key chunks of the split units: per query, m = max_c m_c, w_c = 2^((m_c - m) log2(e)/sqrt(128)),
+// Merge of the key chunks of the split units: per query, m = max_c m_c, w_c = 2^(m_c - m) (offsets in log2 units),
 // O = (sum_c w_c O_c) / (sum_c w_c l_c): the softmax over all keys, exactly as one pass would form it.
 // One 256-thread workgroup per (unit, 2 queries), one thread per output element.
 __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
@@ -418,28 +490,38 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   float l = 0.f, acc = 0.f;
   for (int c = 0; c < a.split; ++c) {
     const int64_t r = (w0 + c) * QB + q;
-    const float w = __builtin_amdgcn_exp2f((a.part_ml[r * 2] - m) * a.scale_log2);
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[r * 2] - m);
     l = fmaf(a.part_ml[r * 2 + 1], w, l);
     acc = fmaf(a.part_o[r * 128 + d], w, acc);
   }
-  a.o[((int64_t)b * a.Lq + qi) * a.ldo + h * 128 + d] = (bf16_t)(pack_bf16x2(acc / l, 0.f) & 0xFFFFu);
+  bf16_t* op = a.o + ((int64_t)b * a.Lq + qi) * a.ldo + h * 128 + d;
+  const float prev = a.accumulate ? bf16_to_f32(*op) : 0.f;
+  *op = (bf16_t)(pack_bf16x2(acc / l + prev, 0.f) & 0xFFFFu);
 }
 
 }  // namespace
 
-int64_t attention_workspace_bytes() { return (int64_t)ATTN_SPLIT_MAX * QB * (128 + 2) * 4; }
+// Workspace: key-split partial outputs [ATTN_SPLIT_MAX][256][128] fp32, their (m, l) [ATTN_SPLIT_MAX][256][2],
+// then the redo flags: 4 per workgroup of the regular launch and of the key-split launch.
+int64_t attention_workspace_bytes(int64_t B, int64_t Lq, int nh) {
+  const int64_t units = B * nh * ceil_div(Lq, QB);
+  return (int64_t)ATTN_SPLIT_MAX * QB * (128 + 2) * 4 + 16 * (units + ATTN_SPLIT_MAX);
+}
 
 hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
                             bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, bool self_attn,
-                            hipStream_t s, float* ws, int64_t ws_bytes) {
+                            hipStream_t s, float* ws, int64_t ws_bytes, bool q_prescaled, bool accumulate) {
   if (B <= 0 || Lq <= 0) return hipSuccess;
   if (Lkv <= 0 || ldv < round_up(Lkv, KT)) return hipErrorInvalidValue;
+  if (ws != nullptr && ws_bytes < attention_workspace_bytes(B, Lq, nh)) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.vt = vt; a.ldv = ldv; a.o = o; a.ldo = ldo;
   a.Lq = Lq; a.Lkv = Lkv; a.nh = nh; a.B = (int)B;
   a.q_tiles = (int)ceil_div(Lq, QB);
   a.scale_log2 = (float)(1.4426950408889634 / sqrt(128.0));
-  a.split = 1; a.units_base = 0; a.chunk = Lkv; a.part_o = nullptr; a.part_ml = nullptr;
+  a.q_mul = q_prescaled ? 1.0f : a.scale_log2;
+  a.split = 1; a.units_base = 0; a.chunk = Lkv; a.part_o = nullptr; a.part_ml = nullptr; a.flags = nullptr;
+  a.accumulate = accumulate ? 1 : 0;
   const int64_t units = (int64_t)a.q_tiles * nh * B;
   // One workgroup per CU at a time: the last round holds units % CUs workgroups.  When it is at most half
   // full, its units are split over key chunks (multiples of 64 keys) so that it fills the chip, and a
@@ -454,22 +536,34 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
   if (ws != nullptr && tail > 0 && 2 * tail <= n_cu) {
     chunk = round_up(ceil_div(Lkv, n_cu / tail), KT);
     split = ceil_div(Lkv, chunk);
-    if (split < 2 || tail * split > ATTN_SPLIT_MAX || ws_bytes < attention_workspace_bytes()) split = 1;
+    if (split < 2 || tail * split > ATTN_SPLIT_MAX) split = 1;
   }
-  auto launch = [&](auto self_tag, auto part_tag, int64_t grid) {
+  auto launch = [&](auto self_tag, auto part_tag, auto exact_tag, int64_t grid) {
     constexpr bool SELF = decltype(self_tag)::value, PART = decltype(part_tag)::value;
-    if (grid > 0) hipLaunchKernelGGL((k_flash_attn<SELF, PART>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    constexpr bool EXACT = decltype(exact_tag)::value;
+    if (grid > 0) hipLaunchKernelGGL((k_flash_attn<SELF, PART, EXACT>), dim3((unsigned)grid), dim3(256), 0, s, a);
   };
-  using T = std::true_type;
-  using F = std::false_type;
+  // with a workspace: the offset-free kernel, then the exact kernel on the workgroups it flagged;
+  // without one: the exact kernel alone
+  auto run = [&](auto part_tag, int64_t grid) {
+    using T = std::true_type;
+    using F = std::false_type;
+    if (a.flags != nullptr) {
+      if (self_attn) launch(T{}, part_tag, F{}, grid);
+      else launch(F{}, part_tag, F{}, grid);
+    }
+    if (self_attn) launch(T{}, part_tag, T{}, grid);
+    else launch(F{}, part_tag, T{}, grid);
+  };
+  unsigned* flags = ws ? (unsigned*)(ws + (int64_t)ATTN_SPLIT_MAX * QB * (128 + 2)) : nullptr;
   a.units = (int)(split > 1 ? units - tail : units);
-  if (self_attn) launch(T{}, F{}, a.units);
-  else launch(F{}, F{}, a.units);
+  a.flags = flags;
+  run(std::false_type{}, a.units);
   if (split > 1) {
     a.split = (int)split; a.units_base = a.units; a.chunk = chunk;
     a.part_o = ws; a.part_ml = ws + (int64_t)ATTN_SPLIT_MAX * QB * 128;
-    if (self_attn) launch(T{}, T{}, tail * split);
-    else launch(F{}, T{}, tail * split);
+    a.flags = flags + 4 * units;
+    run(std::true_type{}, tail * split);
     hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(tail * (QB / 2))), dim3(256), 0, s, a);
   }
   return hipGetLastError();

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void k_ln_mod2(LnArgs a) {
 // ---------------------------------------------------------------------------------------------------
 struct RmsArgs {
   bf16_t* buf; int64_t ld; int64_t rows; int64_t D; float eps;
-  int64_t off_a; const float* gamma_a;
+  int64_t off_a; const float* gamma_a; float scale_a;   // segment a's outputs are also multiplied by scale_a
   int64_t off_b; const float* gamma_b;   // gamma_b == nullptr: single segment
   const float* rope;                     // nullptr: no rotation.  Layout from launch_rope_table.
   int64_t L; int Hp, Wp; int pt, ph;     // tokens per sample, grid, pairs per axis (t, h)
@@ -229,8 +229,8 @@ __device__ __forceinline__ void rms_load(const bf16_t* p, int lane, u32x4 (&raw)
 }
 
 template <int NV, bool ROPE>
-__device__ __forceinline__ void rms_finish(const RmsArgs& a, bf16_t* p, const float* gamma, int lane, const RopeCoef& rc,
-                                           const u32x4 (&raw)[NV]) {
+__device__ __forceinline__ void rms_finish(const RmsArgs& a, bf16_t* p, const float* gamma, float scale, int lane,
+                                           const RopeCoef& rc, const u32x4 (&raw)[NV]) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i)
@@ -239,7 +239,7 @@ __device__ __forceinline__ void rms_finish(const RmsArgs& a, bf16_t* p, const fl
       float lo = lo_bf16(raw[i][e]), hi = hi_bf16(raw[i][e]);
       s += lo * lo + hi * hi;
     }
-  const float rstd = 1.0f / sqrtf(wave_sum(s) / (float)a.D + a.eps);
+  const float rstd = scale / sqrtf(wave_sum(s) / (float)a.D + a.eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c0 = 8 * (lane + 64 * i);
@@ -282,22 +282,22 @@ __global__ __launch_bounds__(256) void k_rms_rope(RmsArgs a) {
     rms_load<NV, true>(r + a.off_b, lane, rb);
     if (a.rope) {
       const RopeCoef rc = rope_coef(a, lane, tf, th, tw);
-      rms_finish<NV, true>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
-      rms_finish<NV, true>(a, r + a.off_b, a.gamma_b, lane, rc, rb);
+      rms_finish<NV, true>(a, r + a.off_a, a.gamma_a, a.scale_a, lane, rc, ra);
+      rms_finish<NV, true>(a, r + a.off_b, a.gamma_b, 1.0f, lane, rc, rb);
     } else {
       const RopeCoef rc = {};
-      rms_finish<NV, false>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
-      rms_finish<NV, false>(a, r + a.off_b, a.gamma_b, lane, rc, rb);
+      rms_finish<NV, false>(a, r + a.off_a, a.gamma_a, a.scale_a, lane, rc, ra);
+      rms_finish<NV, false>(a, r + a.off_b, a.gamma_b, 1.0f, lane, rc, rb);
     }
   } else {
     u32x4 ra[NV];
     rms_load<NV, false>(r + a.off_a, lane, ra);
     if (a.rope) {
       const RopeCoef rc = rope_coef(a, lane, tf, th, tw);
-      rms_finish<NV, true>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
+      rms_finish<NV, true>(a, r + a.off_a, a.gamma_a, a.scale_a, lane, rc, ra);
     } else {
       const RopeCoef rc = {};
-      rms_finish<NV, false>(a, r + a.off_a, a.gamma_a, lane, rc, ra);
+      rms_finish<NV, false>(a, r + a.off_a, a.gamma_a, a.scale_a, lane, rc, ra);
     }
   }
 }
@@ -412,12 +412,12 @@ hipError_t launch_layernorm(float* x, int64_t rows, int64_t D, float eps, int mo
 
 hipError_t launch_rms_rope(bf16_t* buf, int64_t ld, int64_t rows, int64_t D, float eps, int64_t off_a,
                            const float* gamma_a, int64_t off_b, const float* gamma_b, const float* rope, int64_t L,
-                           int Fp, int Hp, int Wp, int dt, int dh, int dw, hipStream_t s) {
+                           int Fp, int Hp, int Wp, int dt, int dh, int dw, hipStream_t s, float scale_a) {
   if (rows <= 0) return hipSuccess;
   if (D % 512 != 0 || D / 512 > 24) return hipErrorInvalidValue;
   RmsArgs a;
   a.buf = buf; a.ld = ld; a.rows = rows; a.D = D; a.eps = eps;
-  a.off_a = off_a; a.gamma_a = gamma_a; a.off_b = off_b; a.gamma_b = gamma_b;
+  a.off_a = off_a; a.gamma_a = gamma_a; a.scale_a = scale_a; a.off_b = off_b; a.gamma_b = gamma_b;
   a.rope = rope; a.L = L > 0 ? L : 1; a.Hp = Hp; a.Wp = Wp; a.pt = dt / 2; a.ph = dh / 2;
   a.rope_h_off = (int64_t)Fp * (dt / 2);
   a.rope_w_off = a.rope_h_off + (int64_t)Hp * (dh / 2);

@@ -71,6 +71,36 @@ __global__ void k_unpatchify(const float* __restrict__ z, int64_t ldz, int64_t B
   }
 }
 
+// Denoising step fused into the unpatchify scatter (Wan2.1 walk-through page, section 7: the guided velocity
+// v_u + s (v_c - v_u) and the Euler update x + (sigma_next - sigma) v; section 6.3 works one step by hand).
+// z holds 2L proj_out rows, the conditional batch element first; x is the model input [1, C_x, F, Hz, Wz]
+// whose first C channels are the noisy sample.  One thread per output element, fp32 arithmetic.
+template <typename T>
+__global__ void k_cfg_euler(const float* __restrict__ z, int64_t ldz, int64_t C, int64_t F, int64_t Hz, int64_t Wz,
+                            const T* __restrict__ x, float scale, float dsigma, T* __restrict__ out) {
+  const int64_t Hp = Hz / 2, Wp = Wz / 2, L = F * Hp * Wp;
+  const int64_t total = C * F * Hz * Wz;
+  for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t xx = idx % Wz;
+    int64_t r = idx / Wz;
+    const int64_t yy = r % Hz; r /= Hz;
+    const int64_t f = r % F;
+    const int64_t c = r / F;
+    const int64_t n = (f * Hp + (yy >> 1)) * Wp + (xx >> 1);
+    const int64_t col = (2 * (yy & 1) + (xx & 1)) * C + c;
+    const float vc = z[n * ldz + col], vu = z[(L + n) * ldz + col];
+    const float v = fmaf(scale, vc - vu, vu);
+    const int64_t xi = ((c * F + f) * Hz + yy) * Wz + xx;   // channel c < C of batch element 0 of the input
+    float xv;
+    if constexpr (sizeof(T) == 2) xv = bf16_to_f32(x[xi]);
+    else xv = x[xi];
+    const float o = fmaf(dsigma, v, xv);
+    if constexpr (sizeof(T) == 2) out[idx] = f32_to_bf16(o);
+    else out[idx] = o;
+  }
+}
+
 // src (fp32 or bf16, rows x cols, leading dim lds) -> bf16 dst (leading dim ldd); columns
 // [cols, ldd) of each written row are zero-filled.
 template <typename T>
@@ -132,6 +162,20 @@ hipError_t launch_unpatchify(const float* z, int64_t ldz, int64_t B, int64_t C, 
   else
     hipLaunchKernelGGL(k_unpatchify<float>, dim3(grid_for(total)), dim3(256), 0, s, z, ldz, B, C, F, Hz, Wz,
                        (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_cfg_euler(const float* z, int64_t ldz, int64_t C, int64_t F, int64_t Hz, int64_t Wz, const void* x,
+                            int dtype, float scale, float sigma, float sigma_next, void* out, hipStream_t s) {
+  const int64_t total = C * F * Hz * Wz;
+  if (total == 0) return hipSuccess;
+  const float ds = sigma_next - sigma;
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_cfg_euler<bf16_t>, dim3(grid_for(total)), dim3(256), 0, s, z, ldz, C, F, Hz, Wz,
+                       (const bf16_t*)x, scale, ds, (bf16_t*)out);
+  else
+    hipLaunchKernelGGL(k_cfg_euler<float>, dim3(grid_for(total)), dim3(256), 0, s, z, ldz, C, F, Hz, Wz,
+                       (const float*)x, scale, ds, (float*)out);
   return hipGetLastError();
 }
 

@@ -12,10 +12,12 @@
 //   head: [x += gate2 * ffn] LN + (table + temb) modulation -> proj_out GEMM -> unpatchify
 // Each residual add [..] runs inside the LayerNorm kernel that follows it: the branch's last Linear
 // writes bf16 (as the branch outputs are in the bf16 model), and x stays fp32.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -49,6 +51,8 @@ struct BlockW {
   bf16_t *wqkv, *wo, *wq2, *wkv2, *wo2, *w1, *w2;
   float *bqkv, *bo, *bq2, *bkv2, *bo2, *b1, *b2;
   float *gq, *gk, *gq2, *gk2, *n2w, *n2b, *table;
+  bf16_t* wkvi;   // image branch: [add_k_proj; add_v_proj] [2D, D]
+  float *bkvi, *gki;
 };
 
 // Bump allocator over one device allocation (256-byte aligned slices).
@@ -77,13 +81,17 @@ struct wan_dit {
   bf16_t* w_pe; float* b_pe;
   float *t_w1, *t_b1, *t_w2, *t_b2, *t_wp, *t_bp;
   bf16_t *c_w1, *c_w2; float *c_b1, *c_b2;
+  bf16_t *i_w1, *i_w2; float *i_b1, *i_b2;   // image MLP (max_image_len > 0)
+  int64_t kp_img = 0;
   std::vector<BlockW> blocks;
   float* head_table; bf16_t* w_out; float* b_out;
   // workspace
   bf16_t *P, *y, *qkv, *vt, *attn, *br, *hbuf, *text_bf, *ctx_h, *ctx, *kv2, *vt2;
-  float *x, *z, *t_s, *t_h, *temb, *tproj, *rope;
-  float* attn_ws;   // key-split partials of the attention's last round
-  int64_t ldv_max, ldv2_max, rows_max, trows_max;
+  bf16_t *img_bf, *img_h, *img_ctx, *kvi, *vti;   // image branch
+  float *x, *z, *t_s, *t_h, *temb, *tproj, *rope, *t_dup;
+  float* attn_ws;   // key-split partials of the attention's last round and its redo flags
+  int64_t attn_ws_bytes = 0;
+  int64_t ldv_max, ldv2_max, ldvi_max, rows_max, trows_max;
   // opt-in timing of the self-attention launches (wan_dit_time_attention): event pairs, start then end
   std::vector<hipEvent_t> att_ev;
   int64_t att_used = 0;
@@ -128,6 +136,9 @@ wan_status check_config(const wan_dit_config* c) {
   if (!(c->rope_theta > 1.0)) return fail(WAN_ERR_INVALID_ARG, "rope_theta must be > 1");
   if (c->max_batch <= 0 || c->max_tokens <= 0 || c->max_text_len <= 0)
     return fail(WAN_ERR_INVALID_ARG, "max_batch, max_tokens and max_text_len must be positive");
+  if (c->max_image_len < 0) return fail(WAN_ERR_INVALID_ARG, "max_image_len must be >= 0");
+  if (c->max_image_len > 0 && (c->image_dim <= 0 || c->image_dim % 8 != 0))
+    return fail(WAN_ERR_UNSUPPORTED, "image_dim must be a positive multiple of 8 (got %d)", c->image_dim);
   return WAN_OK;
 }
 
@@ -150,6 +161,10 @@ std::vector<Expect> expected_weights(const wan_dit_config& c) {
   lin("time_proj", 6 * D, D);
   lin("text_embedder.linear_1", D, c.text_dim);
   lin("text_embedder.linear_2", D, D);
+  if (c.max_image_len > 0) {
+    lin("image_embedder.linear_1", D, c.image_dim);
+    lin("image_embedder.linear_2", D, D);
+  }
   for (int k = 0; k < c.num_layers; ++k) {
     const std::string p = "blocks." + std::to_string(k) + ".";
     e.push_back({p + "scale_shift_table", {1, 6, D}});
@@ -157,6 +172,11 @@ std::vector<Expect> expected_weights(const wan_dit_config& c) {
       for (const char* pr : {"to_q", "to_k", "to_v", "to_out"}) lin(p + a + "." + pr, D, D);
       e.push_back({p + a + ".norm_q.weight", {D}});
       e.push_back({p + a + ".norm_k.weight", {D}});
+    }
+    if (c.max_image_len > 0) {
+      lin(p + "attn2.add_k_proj", D, D);
+      lin(p + "attn2.add_v_proj", D, D);
+      e.push_back({p + "attn2.norm_added_k.weight", {D}});
     }
     e.push_back({p + "norm2.weight", {D}});
     e.push_back({p + "norm2.bias", {D}});
@@ -179,6 +199,9 @@ void plan_weights(wan_dit* h, Arena& ar) {
   h->t_wp = ar.take<float>(6 * D * D); h->t_bp = ar.take<float>(6 * D);
   h->c_w1 = ar.take<bf16_t>(D * c.text_dim); h->c_b1 = ar.take<float>(D);
   h->c_w2 = ar.take<bf16_t>(D * D); h->c_b2 = ar.take<float>(D);
+  const bool img = c.max_image_len > 0;
+  h->i_w1 = img ? ar.take<bf16_t>(D * h->kp_img) : nullptr; h->i_b1 = img ? ar.take<float>(D) : nullptr;
+  h->i_w2 = img ? ar.take<bf16_t>(D * D) : nullptr; h->i_b2 = img ? ar.take<float>(D) : nullptr;
   h->blocks.resize(c.num_layers);
   for (auto& b : h->blocks) {
     b.wqkv = ar.take<bf16_t>(3 * D * D); b.bqkv = ar.take<float>(3 * D);
@@ -191,6 +214,9 @@ void plan_weights(wan_dit* h, Arena& ar) {
     b.gq = ar.take<float>(D); b.gk = ar.take<float>(D); b.gq2 = ar.take<float>(D); b.gk2 = ar.take<float>(D);
     b.n2w = ar.take<float>(D); b.n2b = ar.take<float>(D);
     b.table = ar.take<float>(6 * D);
+    b.wkvi = img ? ar.take<bf16_t>(2 * D * D) : nullptr;
+    b.bkvi = img ? ar.take<float>(2 * D) : nullptr;
+    b.gki = img ? ar.take<float>(D) : nullptr;
   }
   h->head_table = ar.take<float>(2 * D);
   h->w_out = ar.take<bf16_t>(h->n_out * D);
@@ -226,7 +252,16 @@ void plan_workspace(wan_dit* h, Arena& ar) {
   h->ctx = ar.take<bf16_t>(Tx * D);
   h->kv2 = ar.take<bf16_t>(Tx * 2 * D);
   h->vt2 = ar.take<bf16_t>(c.max_batch * D * h->ldv2_max);
-  h->attn_ws = ar.take<float>(attention_workspace_bytes() / 4);
+  const int64_t Ix = c.max_batch * c.max_image_len;
+  h->ldvi_max = round_up(c.max_image_len, 64);
+  h->img_bf = ar.take<bf16_t>(Ix * h->kp_img);
+  h->img_h = ar.take<bf16_t>(Ix * D);
+  h->img_ctx = ar.take<bf16_t>(Ix * D);
+  h->kvi = ar.take<bf16_t>(Ix * 2 * D);
+  h->vti = ar.take<bf16_t>(c.max_image_len ? c.max_batch * D * h->ldvi_max : 0);
+  h->t_dup = ar.take<float>(c.max_batch * (c.per_token_timestep ? c.max_tokens : 1));
+  h->attn_ws_bytes = attention_workspace_bytes(c.max_batch, c.max_tokens, c.num_heads);
+  h->attn_ws = ar.take<float>(h->attn_ws_bytes / 4);
 }
 
 void release_events(wan_dit* h) {
@@ -352,6 +387,7 @@ extern "C" wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight
   (void)hipGetDevice(&h->device);
   h->kp_pe = round_up(4LL * cfg->in_channels, 64);
   h->n_out = 4LL * cfg->out_channels;
+  h->kp_img = cfg->max_image_len > 0 ? round_up(cfg->image_dim, 64) : 0;
   Arena plan_w, plan_ws;
   plan_weights(h, plan_w);
   plan_workspace(h, plan_ws);
@@ -394,6 +430,12 @@ extern "C" wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight
   chk(pack_f("text_embedder.linear_1.bias", h->c_b1));
   chk(pack_lin("text_embedder.linear_2.weight", h->c_w2, D, D, D));
   chk(pack_f("text_embedder.linear_2.bias", h->c_b2));
+  if (cfg->max_image_len > 0) {
+    chk(pack_lin("image_embedder.linear_1.weight", h->i_w1, D, cfg->image_dim, h->kp_img));
+    chk(pack_f("image_embedder.linear_1.bias", h->i_b1));
+    chk(pack_lin("image_embedder.linear_2.weight", h->i_w2, D, D, D));
+    chk(pack_f("image_embedder.linear_2.bias", h->i_b2));
+  }
   for (int k = 0; k < cfg->num_layers; ++k) {
     const std::string p = "blocks." + std::to_string(k) + ".";
     BlockW& b = h->blocks[k];
@@ -416,6 +458,13 @@ extern "C" wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight
     chk(pack_f(p + "attn2.norm_q.weight", b.gq2)); chk(pack_f(p + "attn2.norm_k.weight", b.gk2));
     chk(pack_f(p + "norm2.weight", b.n2w)); chk(pack_f(p + "norm2.bias", b.n2b));
     chk(pack_f(p + "scale_shift_table", b.table));
+    if (cfg->max_image_len > 0) {
+      chk(pack_lin(p + "attn2.add_k_proj.weight", b.wkvi, D, D, D));
+      chk(pack_lin(p + "attn2.add_v_proj.weight", b.wkvi + D * D, D, D, D));
+      chk(pack_f(p + "attn2.add_k_proj.bias", b.bkvi));
+      chk(pack_f(p + "attn2.add_v_proj.bias", b.bkvi + D));
+      chk(pack_f(p + "attn2.norm_added_k.weight", b.gki));
+    }
   }
   chk(pack_f("scale_shift_table", h->head_table));
   chk(pack_lin("proj_out.weight", h->w_out, h->n_out, D, D));
@@ -429,86 +478,155 @@ extern "C" wan_status wan_dit_create(const wan_dit_config* cfg, const wan_weight
   return WAN_OK;
 }
 
-extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
-                                      const wan_tensor* text, wan_tensor* out, void* hip_stream) {
-  g_err.clear();
-  if (!h) return fail(WAN_ERR_INVALID_ARG, "handle is NULL");
+namespace {
+
+// One forward's inputs after validation.  dup: the latent, timestep and image tensors hold batch element 0
+// only, used for every batch element (the CFG pair of a denoising step).
+struct FwdIn {
+  int64_t B, Cin, F, Hz, Wz, Fp, Hp, Wp, L, Lt, Li;
+  const void* latent; int lat_dtype;
+  const float* t; bool per_tok;
+  const void* text; int text_dtype;
+  const void* image; int image_dtype;   // image == nullptr: no image tokens
+  bool dup;
+};
+
+// How the proj_out values leave: unpatchified into out, or (denoising step) CFG-combined and Euler-stepped.
+struct FwdOut {
+  void* out; int dtype;
+  bool step; float scale, sigma, sigma_next;
+};
+
+wan_status check_device(const wan_dit* h) {
+  int dev = -1;
+  (void)hipGetDevice(&dev);
+  if (dev != h->device) return fail(WAN_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
+  return WAN_OK;
+}
+
+// Validate latent / timestep / text (and image) against the configuration; B_in is the batch the tensors
+// hold (1 for a denoising step), in.B the batch the forward runs.
+wan_status check_inputs(const wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep, const wan_tensor* text,
+                        const wan_tensor* image, int64_t B_in, int64_t B_text, FwdIn& in) {
   wan_status st;
   if ((st = check_tensor(latent, "latent")) != WAN_OK) return st;
   if ((st = check_tensor(timestep, "timestep")) != WAN_OK) return st;
   if ((st = check_tensor(text, "text_emb")) != WAN_OK) return st;
-  if ((st = check_tensor(out, "out")) != WAN_OK) return st;
+  if (image && (st = check_tensor(image, "image_emb")) != WAN_OK) return st;
   const wan_dit_config& c = h->cfg;
   if (latent->ndim != 5) return fail(WAN_ERR_SHAPE, "latent must be [B, C, F, H, W]");
-  const int64_t B = latent->shape[0], Cin = latent->shape[1], F = latent->shape[2], Hz = latent->shape[3],
-                Wz = latent->shape[4];
-  if (Cin != c.in_channels) return fail(WAN_ERR_SHAPE, "latent has %lld channels, config expects %d", (long long)Cin, c.in_channels);
-  if (Hz % 2 || Wz % 2) return fail(WAN_ERR_SHAPE, "latent height and width must be even (got %lld x %lld)", (long long)Hz, (long long)Wz);
-  const int64_t Fp = F, Hp = Hz / 2, Wp = Wz / 2, L = Fp * Hp * Wp;
-  if (Fp > 1024 || Hp > 1024 || Wp > 1024)
-    return fail(WAN_ERR_SHAPE, "token grid %lldx%lldx%lld exceeds the 1024 rotary positions per axis", (long long)Fp,
-                (long long)Hp, (long long)Wp);
-  if (B > c.max_batch) return fail(WAN_ERR_SHAPE, "batch %lld > max_batch %lld", (long long)B, (long long)c.max_batch);
-  if (L > c.max_tokens) return fail(WAN_ERR_SHAPE, "%lld tokens > max_tokens %lld", (long long)L, (long long)c.max_tokens);
+  in.Cin = latent->shape[1]; in.F = latent->shape[2]; in.Hz = latent->shape[3]; in.Wz = latent->shape[4];
+  if (B_in < 0 ? false : latent->shape[0] != B_in)
+    return fail(WAN_ERR_SHAPE, "latent batch must be %lld, got %lld", (long long)B_in, (long long)latent->shape[0]);
+  const int64_t B = latent->shape[0];
+  if (in.Cin != c.in_channels)
+    return fail(WAN_ERR_SHAPE, "latent has %lld channels, config expects %d", (long long)in.Cin, c.in_channels);
+  if (in.Hz % 2 || in.Wz % 2)
+    return fail(WAN_ERR_SHAPE, "latent height and width must be even (got %lld x %lld)", (long long)in.Hz, (long long)in.Wz);
+  in.Fp = in.F; in.Hp = in.Hz / 2; in.Wp = in.Wz / 2; in.L = in.Fp * in.Hp * in.Wp;
+  if (in.Fp > 1024 || in.Hp > 1024 || in.Wp > 1024)
+    return fail(WAN_ERR_SHAPE, "token grid %lldx%lldx%lld exceeds the 1024 rotary positions per axis", (long long)in.Fp,
+                (long long)in.Hp, (long long)in.Wp);
+  if (in.B > c.max_batch) return fail(WAN_ERR_SHAPE, "batch %lld > max_batch %lld", (long long)in.B, (long long)c.max_batch);
+  if (in.L > c.max_tokens) return fail(WAN_ERR_SHAPE, "%lld tokens > max_tokens %lld", (long long)in.L, (long long)c.max_tokens);
   // timestep
   if (timestep->dtype != WAN_F32) return fail(WAN_ERR_DTYPE, "timestep must be WAN_F32");
-  bool per_tok;
-  if (timestep->ndim == 1 && timestep->shape[0] == B) per_tok = false;
-  else if (timestep->ndim == 2 && timestep->shape[0] == B && timestep->shape[1] == L) per_tok = true;
-  else return fail(WAN_ERR_SHAPE, "timestep must be [B] or [B, L] (B=%lld, L=%lld), got %s", (long long)B, (long long)L,
+  if (timestep->ndim == 1 && timestep->shape[0] == B) in.per_tok = false;
+  else if (timestep->ndim == 2 && timestep->shape[0] == B && timestep->shape[1] == in.L) in.per_tok = true;
+  else return fail(WAN_ERR_SHAPE, "timestep must be [B] or [B, L] (B=%lld, L=%lld), got %s", (long long)B, (long long)in.L,
                    shape_str(timestep->shape, timestep->ndim).c_str());
-  if (per_tok && !c.per_token_timestep)
+  if (in.per_tok && !c.per_token_timestep)
     return fail(WAN_ERR_UNSUPPORTED, "per-token timesteps need per_token_timestep = 1 in the config");
   // text
-  if (text->ndim != 3 || text->shape[0] != B || text->shape[2] != c.text_dim)
-    return fail(WAN_ERR_SHAPE, "text_emb must be [B, Lt, %d], got %s", c.text_dim, shape_str(text->shape, text->ndim).c_str());
-  const int64_t Lt = text->shape[1];
-  if (B > 0 && (Lt < 1 || Lt > c.max_text_len))
-    return fail(WAN_ERR_SHAPE, "text length %lld outside [1, %lld]", (long long)Lt, (long long)c.max_text_len);
-  if (text->dtype == WAN_BF16 && ((uintptr_t)text->data & 15))
-    return fail(WAN_ERR_INVALID_ARG, "bf16 text_emb must be 16-byte aligned");
-  // out
-  if (out->ndim != 5 || out->shape[0] != B || out->shape[1] != c.out_channels || out->shape[2] != F || out->shape[3] != Hz ||
-      out->shape[4] != Wz)
-    return fail(WAN_ERR_SHAPE, "out must be [B, %d, F, H, W] matching the latent, got %s", c.out_channels,
-                shape_str(out->shape, out->ndim).c_str());
-  if (out->dtype != latent->dtype) return fail(WAN_ERR_DTYPE, "out dtype must match the latent dtype");
-  int dev = -1;
-  (void)hipGetDevice(&dev);
-  if (dev != h->device) return fail(WAN_ERR_INVALID_ARG, "current device %d is not the handle's device %d", dev, h->device);
-  if (B == 0 || L == 0) return WAN_OK;
+  if (text->ndim != 3 || text->shape[0] != B_text || text->shape[2] != c.text_dim)
+    return fail(WAN_ERR_SHAPE, "text_emb must be [%lld, Lt, %d], got %s", (long long)B_text, c.text_dim,
+                shape_str(text->shape, text->ndim).c_str());
+  in.Lt = text->shape[1];
+  if (in.B > 0 && (in.Lt < 1 || in.Lt > c.max_text_len))
+    return fail(WAN_ERR_SHAPE, "text length %lld outside [1, %lld]", (long long)in.Lt, (long long)c.max_text_len);
+  if (text->dtype == WAN_BF16 && ((uintptr_t)text->data & 15)) return fail(WAN_ERR_INVALID_ARG, "bf16 text_emb must be 16-byte aligned");
+  // image tokens
+  in.Li = 0;
+  in.image = nullptr;
+  if (image) {
+    if (c.max_image_len == 0) return fail(WAN_ERR_UNSUPPORTED, "image tokens need max_image_len > 0 in the config");
+    if (image->ndim != 3 || image->shape[0] != B || image->shape[2] != c.image_dim)
+      return fail(WAN_ERR_SHAPE, "image_emb must be [%lld, Li, %d], got %s", (long long)B, c.image_dim,
+                  shape_str(image->shape, image->ndim).c_str());
+    in.Li = image->shape[1];
+    if (in.B > 0 && (in.Li < 1 || in.Li > c.max_image_len))
+      return fail(WAN_ERR_SHAPE, "image length %lld outside [1, %lld]", (long long)in.Li, (long long)c.max_image_len);
+    if (image->dtype == WAN_BF16 && ((uintptr_t)image->data & 15))
+      return fail(WAN_ERR_INVALID_ARG, "bf16 image_emb must be 16-byte aligned");
+    in.image = image->data;
+    in.image_dtype = image->dtype;
+  }
+  in.latent = latent->data; in.lat_dtype = latent->dtype;
+  in.t = (const float*)timestep->data;
+  in.text = text->data; in.text_dtype = text->dtype;
+  return check_device(h);
+}
 
-  hipStream_t s = (hipStream_t)hip_stream;
+// Enqueue one forward (forward sequence in the file header).
+wan_status enqueue_forward(wan_dit* h, const FwdIn& in, const FwdOut& fo, hipStream_t s) {
+  const wan_dit_config& c = h->cfg;
+  const int64_t B = in.B, L = in.L, Lt = in.Lt, Li = in.Li, F = in.F, Hz = in.Hz, Wz = in.Wz;
   const int64_t D = c.dim, Fd = c.ffn_dim, M = B * L, nh = c.num_heads;
-  const int64_t R = per_tok ? M : B;
-  const int64_t rows_per_mod = per_tok ? 1 : L;
+  const int64_t R = in.per_tok ? M : B;
+  const int64_t rows_per_mod = in.per_tok ? 1 : L;
   const int dt = c.rope_dim_t, dh = c.rope_dim_h, dw = c.rope_dim_w;
-  const int64_t ldv = round_up(L, 64), ldv2 = round_up(Lt, 64);
-  const float eps = c.eps;
+  const int64_t ldv = round_up(L, 64), ldv2 = round_up(Lt, 64), ldvi = round_up(Li, 64);
+  const float eps = c.eps, qs = attention_q_scale();
 
   // 1. patch embedding -> fp32 residual stream x [M, D]
-  HIP_TRY(launch_patchify(latent->data, latent->dtype, B, Cin, F, Hz, Wz, h->kp_pe, h->P, s), "patchify");
+  if (in.dup) {
+    for (int64_t b = 0; b < B; ++b)
+      HIP_TRY(launch_patchify(in.latent, in.lat_dtype, 1, in.Cin, F, Hz, Wz, h->kp_pe, h->P + b * L * h->kp_pe, s), "patchify");
+  } else {
+    HIP_TRY(launch_patchify(in.latent, in.lat_dtype, B, in.Cin, F, Hz, Wz, h->kp_pe, h->P, s), "patchify");
+  }
   HIP_TRY(launch_gemm_bf16(h->P, h->kp_pe, h->w_pe, h->kp_pe, h->b_pe, M, D, h->kp_pe, EPI_F32, h->x, D, nullptr, nullptr,
                            0, 1, s), "patch embed");
   // 2. timestep embedding (fp32)
-  HIP_TRY(launch_sinusoid((const float*)timestep->data, R, c.freq_dim, h->t_s, s), "sinusoid");
+  const float* t = in.t;
+  if (in.dup) {
+    const int64_t per = in.per_tok ? L : 1;
+    for (int64_t b = 0; b < B; ++b)
+      HIP_TRY(hipMemcpyAsync(h->t_dup + b * per, in.t, per * sizeof(float), hipMemcpyDeviceToDevice, s), "timestep copy");
+    t = h->t_dup;
+  }
+  HIP_TRY(launch_sinusoid(t, R, c.freq_dim, h->t_s, s), "sinusoid");
   HIP_TRY(launch_gemm_f32(h->t_s, c.freq_dim, h->t_w1, c.freq_dim, h->t_b1, R, D, c.freq_dim, h->t_h, D, 0, 1, s), "time linear_1");
   HIP_TRY(launch_gemm_f32(h->t_h, D, h->t_w2, D, h->t_b2, R, D, D, h->temb, D, 0, 0, s), "time linear_2");
   HIP_TRY(launch_gemm_f32(h->temb, D, h->t_wp, D, h->t_bp, R, 6 * D, D, h->tproj, 6 * D, 1, 0, s), "time_proj");
   // 3. text projection
-  const bf16_t* txt = (const bf16_t*)text->data;
-  if (text->dtype == WAN_F32) {
-    HIP_TRY(launch_pack_bf16(text->data, WAN_F32, B * Lt, c.text_dim, c.text_dim, h->text_bf, c.text_dim, s), "text cast");
+  const bf16_t* txt = (const bf16_t*)in.text;
+  if (in.text_dtype == WAN_F32) {
+    HIP_TRY(launch_pack_bf16(in.text, WAN_F32, B * Lt, c.text_dim, c.text_dim, h->text_bf, c.text_dim, s), "text cast");
     txt = h->text_bf;
   }
   HIP_TRY(launch_gemm_bf16(txt, c.text_dim, h->c_w1, c.text_dim, h->c_b1, B * Lt, D, c.text_dim, EPI_GELU_BF16, h->ctx_h, D,
                            nullptr, nullptr, 0, 1, s), "text linear_1");
   HIP_TRY(launch_gemm_bf16(h->ctx_h, D, h->c_w2, D, h->c_b2, B * Lt, D, D, EPI_BF16, h->ctx, D, nullptr, nullptr, 0, 1, s),
           "text linear_2");
+  // 3b. image tokens: the same two-layer projection on the CLIP features (batch element 0 copied for dup)
+  if (Li > 0) {
+    const int64_t rows_in = in.dup ? Li : B * Li;
+    HIP_TRY(launch_pack_bf16(in.image, in.image_dtype, rows_in, c.image_dim, c.image_dim, h->img_bf, h->kp_img, s), "image cast");
+    if (in.dup)
+      for (int64_t b = 1; b < B; ++b)
+        HIP_TRY(hipMemcpyAsync(h->img_bf + b * Li * h->kp_img, h->img_bf, Li * h->kp_img * sizeof(bf16_t),
+                               hipMemcpyDeviceToDevice, s), "image copy");
+    HIP_TRY(launch_gemm_bf16(h->img_bf, h->kp_img, h->i_w1, h->kp_img, h->i_b1, B * Li, D, h->kp_img, EPI_GELU_BF16, h->img_h,
+                             D, nullptr, nullptr, 0, 1, s), "image linear_1");
+    HIP_TRY(launch_gemm_bf16(h->img_h, D, h->i_w2, D, h->i_b2, B * Li, D, D, EPI_BF16, h->img_ctx, D, nullptr, nullptr, 0, 1, s),
+            "image linear_2");
+  }
   // 4. rotary tables for this grid
-  HIP_TRY(launch_rope_table(h->rope, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, c.rope_theta, s), "rope table");
+  HIP_TRY(launch_rope_table(h->rope, (int)in.Fp, (int)in.Hp, (int)in.Wp, dt, dh, dw, c.rope_theta, s), "rope table");
 
   // 5. blocks.  res_* describe the pending residual: the previous block's FFN output and its gate.
+  //    Queries leave the QK norm multiplied by the attention's log2(e)/sqrt(128).
   int res_mode = 0;
   const float* res_tab = nullptr;
   const float* res_src = nullptr;
@@ -519,13 +637,13 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
                              rows_per_mod, nullptr, nullptr, res_mode, h->br, res_tab, res_src, 6 * D, h->y, s), "norm1");
     HIP_TRY(launch_gemm_bf16(h->y, D, b.wqkv, D, b.bqkv, M, 3 * D, D, EPI_BF16, h->qkv, 3 * D, nullptr, nullptr, 0, 1, s),
             "qkv");
-    HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)Fp, (int)Hp, (int)Wp, dt, dh, dw, s),
-            "qk norm rope");
+    HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)in.Fp, (int)in.Hp, (int)in.Wp, dt, dh,
+                            dw, s, qs), "qk norm rope");
     HIP_TRY(launch_transpose_v(h->qkv, 3 * D, 2 * D, B, L, (int)nh, h->vt, ldv, s), "v transpose");
     const bool timed = 2 * h->att_used < (int64_t)h->att_ev.size();
     if (timed) HIP_TRY(hipEventRecord(h->att_ev[2 * h->att_used], s), "self attention timing");
     HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s,
-                             h->attn_ws, attention_workspace_bytes()), "self attention");
+                             h->attn_ws, h->attn_ws_bytes, true), "self attention");
     if (timed) HIP_TRY(hipEventRecord(h->att_ev[2 * h->att_used++ + 1], s), "self attention timing");
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn1 out");
     // cross-attention: x += gate1 * attn, then norm2 (affine)
@@ -533,13 +651,23 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
                              b.table + 2 * D, h->tproj + 2 * D, 6 * D, h->y, s), "norm2");
     bf16_t* q2 = h->qkv;
     HIP_TRY(launch_gemm_bf16(h->y, D, b.wq2, D, b.bq2, M, D, D, EPI_BF16, q2, D, nullptr, nullptr, 0, 1, s), "q2");
-    HIP_TRY(launch_rms_rope(q2, D, M, D, eps, 0, b.gq2, 0, nullptr, nullptr, L, 1, 1, 1, dt, dh, dw, s), "q2 norm");
+    HIP_TRY(launch_rms_rope(q2, D, M, D, eps, 0, b.gq2, 0, nullptr, nullptr, L, 1, 1, 1, dt, dh, dw, s, qs), "q2 norm");
     HIP_TRY(launch_gemm_bf16(h->ctx, D, b.wkv2, D, b.bkv2, B * Lt, 2 * D, D, EPI_BF16, h->kv2, 2 * D, nullptr, nullptr, 0, 1, s),
             "kv2");
     HIP_TRY(launch_rms_rope(h->kv2, 2 * D, B * Lt, D, eps, 0, b.gk2, 0, nullptr, nullptr, Lt, 1, 1, 1, dt, dh, dw, s), "k2 norm");
     HIP_TRY(launch_transpose_v(h->kv2, 2 * D, D, B, Lt, (int)nh, h->vt2, ldv2, s), "v2 transpose");
-    HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, false, s,
-                             h->attn_ws, attention_workspace_bytes()), "cross attention");
+    HIP_TRY(launch_attention(q2, D, h->kv2, 2 * D, h->vt2, ldv2, h->attn, D, B, L, Lt, (int)nh, false, s, h->attn_ws,
+                             h->attn_ws_bytes, true), "cross attention");
+    if (Li > 0) {
+      // the image tokens' own keys and values; their attention output is added to the text one
+      HIP_TRY(launch_gemm_bf16(h->img_ctx, D, b.wkvi, D, b.bkvi, B * Li, 2 * D, D, EPI_BF16, h->kvi, 2 * D, nullptr, nullptr, 0,
+                               1, s), "image kv");
+      HIP_TRY(launch_rms_rope(h->kvi, 2 * D, B * Li, D, eps, 0, b.gki, 0, nullptr, nullptr, Li, 1, 1, 1, dt, dh, dw, s),
+              "image k norm");
+      HIP_TRY(launch_transpose_v(h->kvi, 2 * D, D, B, Li, (int)nh, h->vti, ldvi, s), "image v transpose");
+      HIP_TRY(launch_attention(q2, D, h->kvi, 2 * D, h->vti, ldvi, h->attn, D, B, L, Li, (int)nh, false, s, h->attn_ws,
+                               h->attn_ws_bytes, true, true), "image cross attention");
+    }
     HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn2 out");
     // feed-forward: x += cross-attn (ungated), then norm3 + modulation
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 3 * D, b.table + 4 * D, h->tproj, 6 * D, 3 * D, 4 * D,
@@ -556,8 +684,75 @@ extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, cons
                            nullptr, res_mode, h->br, res_tab, res_src, 6 * D, h->y, s), "norm_out");
   HIP_TRY(launch_gemm_bf16(h->y, D, h->w_out, D, h->b_out, M, h->n_out, D, EPI_F32, h->z, h->n_out, nullptr, nullptr, 0, 1, s),
           "proj_out");
-  HIP_TRY(launch_unpatchify(h->z, h->n_out, B, c.out_channels, F, Hz, Wz, out->data, out->dtype, s), "unpatchify");
+  if (fo.step)
+    HIP_TRY(launch_cfg_euler(h->z, h->n_out, c.out_channels, F, Hz, Wz, in.latent, fo.dtype, fo.scale, fo.sigma,
+                             fo.sigma_next, fo.out, s), "cfg + euler step");
+  else
+    HIP_TRY(launch_unpatchify(h->z, h->n_out, B, c.out_channels, F, Hz, Wz, fo.out, fo.dtype, s), "unpatchify");
   return WAN_OK;
+}
+
+wan_status forward_common(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep, const wan_tensor* text,
+                          const wan_tensor* image, wan_tensor* out, void* hip_stream) {
+  if (!h) return fail(WAN_ERR_INVALID_ARG, "handle is NULL");
+  wan_status st;
+  if ((st = check_tensor(latent, "latent")) != WAN_OK) return st;
+  if ((st = check_tensor(out, "out")) != WAN_OK) return st;
+  FwdIn in;
+  in.B = latent->ndim == 5 ? latent->shape[0] : 0;
+  in.dup = false;
+  if ((st = check_inputs(h, latent, timestep, text, image, -1, in.B, in)) != WAN_OK) return st;
+  const wan_dit_config& c = h->cfg;
+  if (out->ndim != 5 || out->shape[0] != in.B || out->shape[1] != c.out_channels || out->shape[2] != in.F ||
+      out->shape[3] != in.Hz || out->shape[4] != in.Wz)
+    return fail(WAN_ERR_SHAPE, "out must be [B, %d, F, H, W] matching the latent, got %s", c.out_channels,
+                shape_str(out->shape, out->ndim).c_str());
+  if (out->dtype != latent->dtype) return fail(WAN_ERR_DTYPE, "out dtype must match the latent dtype");
+  if (in.B == 0 || in.L == 0) return WAN_OK;
+  FwdOut fo{out->data, out->dtype, false, 0.f, 0.f, 0.f};
+  return enqueue_forward(h, in, fo, (hipStream_t)hip_stream);
+}
+
+}  // namespace
+
+extern "C" wan_status wan_dit_forward(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
+                                      const wan_tensor* text, wan_tensor* out, void* hip_stream) {
+  g_err.clear();
+  return forward_common(h, latent, timestep, text, nullptr, out, hip_stream);
+}
+
+extern "C" wan_status wan_dit_forward_image(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
+                                            const wan_tensor* text, const wan_tensor* image, wan_tensor* out,
+                                            void* hip_stream) {
+  g_err.clear();
+  if (!image) return fail(WAN_ERR_INVALID_ARG, "image_emb is NULL (use wan_dit_forward without image tokens)");
+  return forward_common(h, latent, timestep, text, image, out, hip_stream);
+}
+
+extern "C" wan_status wan_dit_denoise_step(wan_dit* h, const wan_tensor* latent, const wan_tensor* timestep,
+                                           const wan_tensor* text_pair, const wan_tensor* image, float guidance_scale,
+                                           float sigma, float sigma_next, wan_tensor* x_next, void* hip_stream) {
+  g_err.clear();
+  if (!h) return fail(WAN_ERR_INVALID_ARG, "handle is NULL");
+  wan_status st;
+  if ((st = check_tensor(x_next, "x_next")) != WAN_OK) return st;
+  if (!std::isfinite(guidance_scale) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return fail(WAN_ERR_INVALID_ARG, "guidance_scale, sigma and sigma_next must be finite");
+  if (h->cfg.max_batch < 2) return fail(WAN_ERR_UNSUPPORTED, "a denoising step runs a batch of 2: max_batch must be >= 2");
+  FwdIn in;
+  in.B = 2;
+  in.dup = true;
+  if ((st = check_inputs(h, latent, timestep, text_pair, image, 1, 2, in)) != WAN_OK) return st;
+  const wan_dit_config& c = h->cfg;
+  if (x_next->ndim != 5 || x_next->shape[0] != 1 || x_next->shape[1] != c.out_channels || x_next->shape[2] != in.F ||
+      x_next->shape[3] != in.Hz || x_next->shape[4] != in.Wz)
+    return fail(WAN_ERR_SHAPE, "x_next must be [1, %d, F, H, W] matching the latent, got %s", c.out_channels,
+                shape_str(x_next->shape, x_next->ndim).c_str());
+  if (x_next->dtype != latent->dtype) return fail(WAN_ERR_DTYPE, "x_next dtype must match the latent dtype");
+  if (x_next->data == latent->data) return fail(WAN_ERR_INVALID_ARG, "x_next must not alias the latent");
+  if (in.L == 0) return WAN_OK;
+  FwdOut fo{x_next->data, x_next->dtype, true, guidance_scale, sigma, sigma_next};
+  return enqueue_forward(h, in, fo, (hipStream_t)hip_stream);
 }
 
 // =====================================================================================================
@@ -589,6 +784,22 @@ extern "C" wan_status wan_op_unpatchify(const float* z, int64_t ldz, int64_t B, 
   REQUIRE(ldz >= 4 * C, WAN_ERR_SHAPE, "unpatchify: ldz < 4C");
   REQUIRE((z && out) || B * F * Hz * Wz == 0, WAN_ERR_INVALID_ARG, "unpatchify: NULL pointer");
   HIP_TRY(launch_unpatchify(z, ldz, B, C, F, Hz, Wz, out, out_dtype, (hipStream_t)stream), "unpatchify");
+  return WAN_OK;
+}
+
+extern "C" wan_status wan_op_cfg_euler(const float* z, int64_t ldz, int64_t C, int64_t F, int64_t Hz, int64_t Wz,
+                                       const void* x, int64_t Cx, int32_t dtype, float guidance_scale, float sigma,
+                                       float sigma_next, void* x_next, void* stream) {
+  g_err.clear();
+  REQUIRE(dtype == WAN_F32 || dtype == WAN_BF16, WAN_ERR_DTYPE, "cfg_euler: bad dtype");
+  REQUIRE(C > 0 && Cx >= C && F >= 0 && Hz >= 0 && Wz >= 0 && Hz % 2 == 0 && Wz % 2 == 0, WAN_ERR_SHAPE, "cfg_euler: bad sizes");
+  REQUIRE(ldz >= 4 * C, WAN_ERR_SHAPE, "cfg_euler: ldz < 4C");
+  REQUIRE((z && x && x_next) || F * Hz * Wz == 0, WAN_ERR_INVALID_ARG, "cfg_euler: NULL pointer");
+  REQUIRE(x != x_next || F * Hz * Wz == 0, WAN_ERR_INVALID_ARG, "cfg_euler: x_next must not alias x");
+  REQUIRE(std::isfinite(guidance_scale) && std::isfinite(sigma) && std::isfinite(sigma_next), WAN_ERR_INVALID_ARG,
+          "cfg_euler: guidance_scale, sigma and sigma_next must be finite");
+  HIP_TRY(launch_cfg_euler(z, ldz, C, F, Hz, Wz, x, dtype, guidance_scale, sigma, sigma_next, x_next, (hipStream_t)stream),
+          "cfg_euler");
   return WAN_OK;
 }
 
@@ -653,7 +864,7 @@ extern "C" wan_status wan_op_rope_table(float* table, int32_t Fp, int32_t Hp, in
 extern "C" wan_status wan_op_qk_norm_rope(void* buf, int64_t ld, int64_t rows, int64_t D, float eps, int64_t off_a,
                                           const float* gamma_a, int64_t off_b, const float* gamma_b, const float* table,
                                           int64_t L, int32_t Fp, int32_t Hp, int32_t Wp, int32_t dt, int32_t dh, int32_t dw,
-                                          void* stream) {
+                                          float scale_a, void* stream) {
   g_err.clear();
   REQUIRE(rows >= 0 && D > 0 && D % 512 == 0 && D <= 12288, WAN_ERR_SHAPE, "qk_norm_rope: D must be a multiple of 512 <= 12288");
   REQUIRE(buf && gamma_a, WAN_ERR_INVALID_ARG, "qk_norm_rope: NULL pointer");
@@ -664,8 +875,9 @@ extern "C" wan_status wan_op_qk_norm_rope(void* buf, int64_t ld, int64_t rows, i
     REQUIRE(dt > 0 && dh > 0 && dw > 0 && !((dt | dh | dw) & 1) && dt + dh + dw == 128, WAN_ERR_SHAPE,
             "qk_norm_rope: rope dims must be even and sum to 128");
   }
+  REQUIRE(std::isfinite(scale_a), WAN_ERR_INVALID_ARG, "qk_norm_rope: scale_a must be finite");
   HIP_TRY(launch_rms_rope((bf16_t*)buf, ld, rows, D, eps, off_a, gamma_a, off_b, gamma_b, table, L, Fp, Hp, Wp, dt, dh, dw,
-                          (hipStream_t)stream), "qk_norm_rope");
+                          (hipStream_t)stream, scale_a), "qk_norm_rope");
   return WAN_OK;
 }
 
@@ -694,7 +906,10 @@ extern "C" wan_status wan_op_attention(const void* q, int64_t ldq, const void* k
   return WAN_OK;
 }
 
-extern "C" int64_t wan_op_attention_workspace_bytes(void) { return attention_workspace_bytes(); }
+extern "C" int64_t wan_op_attention_workspace_bytes(int64_t B, int64_t Lq, int32_t nh) {
+  if (B < 0 || Lq < 0 || nh <= 0) return -1;
+  return attention_workspace_bytes(B, Lq, nh);
+}
 
 extern "C" wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
                                           int64_t ldv, void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh,
@@ -706,9 +921,10 @@ extern "C" wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void
   REQUIRE(ldq % 8 == 0 && ldk % 8 == 0 && ldo % 4 == 0 && ldq >= 128LL * nh && ldk >= 128LL * nh && ldo >= 128LL * nh,
           WAN_ERR_SHAPE, "attention: bad row strides");
   REQUIRE((q && k && vt && o) || B * Lq == 0, WAN_ERR_INVALID_ARG, "attention: NULL pointer");
-  REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 15) == 0 && workspace_bytes >= attention_workspace_bytes(),
+  REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 15) == 0 &&
+              workspace_bytes >= attention_workspace_bytes(B, Lq, nh),
           WAN_ERR_INVALID_ARG, "attention: workspace must be 16-byte aligned and >= %lld bytes",
-          (long long)attention_workspace_bytes());
+          (long long)attention_workspace_bytes(B, Lq, nh));
   HIP_TRY(launch_attention((const bf16_t*)q, ldq, (const bf16_t*)k, ldk, (const bf16_t*)vt, ldv, (bf16_t*)o, ldo, B, Lq, Lkv, nh,
                            Lq == Lkv, (hipStream_t)stream, (float*)workspace, workspace_bytes), "attention");
   return WAN_OK;
