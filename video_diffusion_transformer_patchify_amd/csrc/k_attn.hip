@@ -22,16 +22,19 @@
 //     (O^T += V^T P^T) once the 32 key rows of a K fragment are taken in the order pi(i), which swaps
 //     bits 2 and 3 of i.  With that order, lane half g holds keys 8g..8g+7 (+16) of each 16-key step.
 //   * Keys are processed in 32-key sub-tiles j, software pipelined: the MFMAs of S(j+1) are issued
-//     together with the exp / row-sum / bf16 packing of S(j), and the PV MFMAs of sub-tile j together
-//     with the row max of S(j+1), so matrix and vector work of one wave overlap.
-//   * Softmax in base 2: Q enters the score MFMAs multiplied by log2(e)/sqrt(128), so S is already
-//     in log2 units and a probability is one exp2 of an accumulator value, with no offset: the row's
-//     scores are not reduced to a running max at all while they stay in a safe range (any common
-//     offset of numerator and denominator cancels in the final division).  Each sub-tile's per-lane
-//     probability sum is checked against 2^64, and the first sub-tile's row max against -60; a wave
-//     whose rows leave that range (scores beyond ~60 log2 units) switches, from there on, to the exact online
-//     softmax with a running max m, raised only when a sub-tile's max passes it by more than 8 (the
-//     stale max keeps probabilities below 2^8), rescaling O and l when it is.
+//     together with the exp / row-sum / bf16 packing of S(j), then the PV MFMAs of sub-tile j together
+//     with the copy of S(j+1) out of the accumulator registers, so matrix and vector work of one wave
+//     overlap.
+//   * Softmax in base 2: Q enters the score MFMAs multiplied by log2(e)/sqrt(128), so S is already in
+//     log2 units and a probability is one exp2 of an accumulator value, with no offset at all: the row's
+//     scores are not reduced to a running max while they stay in a safe range (any common offset of
+//     numerator and denominator cancels in the final division).  Each sub-tile's per-lane probability
+//     sum is checked against 2^64 (no overflow anywhere after), and the first sub-tile's row max against
+//     -60 (the largest probability stays a normal float); the check is branch-free, so the loop stays
+//     one block.  A wave whose rows leave that range drops its results and marks its unit; the exact
+//     kernel (same file, EXACT) then recomputes the marked units with the online softmax: a running
+//     max, raised only when a sub-tile's max passes it by more than 8 (the stale max keeps
+//     probabilities below 2^8), rescaling O and l when it is.
 //   * Row sums stay per lane half and are combined once at the end.
 //   * Only the last sub-tile can be partial; its scores are masked in a peeled copy of the loop body.
 #include <type_traits>
@@ -52,7 +55,7 @@ constexpr int TILE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
 constexpr float SUM_LIMIT = 18446744073709551616.0f;   // 2^64: largest per-lane sub-tile sum, offset-free
 constexpr float MAX_FLOOR = -60.0f;                    // smallest first-sub-tile row max, offset-free
 constexpr float RESCALE_LOG2 = 8.0f;                   // exact path: margin before the running max is raised
-constexpr int64_t ATTN_SPLIT_MAX = 256;   // workgroups of a key-split launch (workspace size)
+constexpr int64_t ATTN_SPLIT_MAX = 256;   // workgroups of a key-split launch (default workspace size)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -501,19 +504,21 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
 
 }  // namespace
 
-// Workspace: key-split partial outputs [ATTN_SPLIT_MAX][256][128] fp32, their (m, l) [ATTN_SPLIT_MAX][256][2],
-// then the redo flags: 4 per workgroup of the regular launch and of the key-split launch.
-int64_t attention_workspace_bytes(int64_t B, int64_t Lq, int nh) {
+// Workspace: key-split partial outputs [split_cap][256][128] fp32, their (m, l) [split_cap][256][2], then the
+// redo flags: 4 per workgroup of the regular launch and of the key-split launch.
+int64_t attention_workspace_bytes(int64_t B, int64_t Lq, int nh, int64_t split_cap) {
   const int64_t units = B * nh * ceil_div(Lq, QB);
-  return (int64_t)ATTN_SPLIT_MAX * QB * (128 + 2) * 4 + 16 * (units + ATTN_SPLIT_MAX);
+  return split_cap * QB * (128 + 2) * 4 + 16 * (units + split_cap);
 }
 
 hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
                             bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, bool self_attn,
-                            hipStream_t s, float* ws, int64_t ws_bytes, bool q_prescaled, bool accumulate) {
+                            hipStream_t s, float* ws, int64_t ws_bytes, bool q_prescaled, bool accumulate,
+                            int64_t split_cap) {
   if (B <= 0 || Lq <= 0) return hipSuccess;
   if (Lkv <= 0 || ldv < round_up(Lkv, KT)) return hipErrorInvalidValue;
-  if (ws != nullptr && ws_bytes < attention_workspace_bytes(B, Lq, nh)) return hipErrorInvalidValue;
+  if (split_cap < 1) return hipErrorInvalidValue;
+  if (ws != nullptr && ws_bytes < attention_workspace_bytes(B, Lq, nh, split_cap)) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q; a.ldq = ldq; a.k = k; a.ldk = ldk; a.vt = vt; a.ldv = ldv; a.o = o; a.ldo = ldo;
   a.Lq = Lq; a.Lkv = Lkv; a.nh = nh; a.B = (int)B;
@@ -536,7 +541,7 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
   if (ws != nullptr && tail > 0 && 2 * tail <= n_cu) {
     chunk = round_up(ceil_div(Lkv, n_cu / tail), KT);
     split = ceil_div(Lkv, chunk);
-    if (split < 2 || tail * split > ATTN_SPLIT_MAX) split = 1;
+    if (split < 2 || tail * split > split_cap) split = 1;
   }
   auto launch = [&](auto self_tag, auto part_tag, auto exact_tag, int64_t grid) {
     constexpr bool SELF = decltype(self_tag)::value, PART = decltype(part_tag)::value;
@@ -555,16 +560,17 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
     if (self_attn) launch(T{}, part_tag, T{}, grid);
     else launch(F{}, part_tag, T{}, grid);
   };
-  unsigned* flags = ws ? (unsigned*)(ws + (int64_t)ATTN_SPLIT_MAX * QB * (128 + 2)) : nullptr;
+  unsigned* flags = ws ? (unsigned*)(ws + split_cap * QB * (128 + 2)) : nullptr;
   a.units = (int)(split > 1 ? units - tail : units);
   a.flags = flags;
   run(std::false_type{}, a.units);
   if (split > 1) {
     a.split = (int)split; a.units_base = a.units; a.chunk = chunk;
-    a.part_o = ws; a.part_ml = ws + (int64_t)ATTN_SPLIT_MAX * QB * 128;
+    a.part_o = ws; a.part_ml = ws + split_cap * QB * 128;
     a.flags = flags + 4 * units;
     run(std::true_type{}, tail * split);
     hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(tail * (QB / 2))), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
+

@@ -52,7 +52,8 @@ hipError_t launch_sinusoid(const float* t, int64_t rows, int freq_dim, float* ou
 hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt, int64_t ldv,
                             bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh, bool self_attn,
                             hipStream_t s, float* ws = nullptr, int64_t ws_bytes = 0, bool q_prescaled = false,
-                            bool accumulate = false);
-int64_t attention_workspace_bytes(int64_t B, int64_t Lq, int nh);
+                            bool accumulate = false, int64_t split_cap = 256);
+// split_cap: most workgroups a key-split last round may use (the workspace holds their partial results)
+int64_t attention_workspace_bytes(int64_t B, int64_t Lq, int nh, int64_t split_cap = 256);
 
 hipError_t launch_mfma_probe(float* sink, int blocks, int64_t rounds, int random_operands, hipStream_t s);
