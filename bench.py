@@ -165,7 +165,7 @@ def probe(cfg):
     vt = Bd.op_transpose_v(qkv, 2 * D, B, L, nh, ldv)
     out = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
-    Bd.op_attention(qkv, qkv[:, D:], vt, out, B, L, L, nh)
+    Bd.op_attention_ws(qkv, qkv[:, D:], vt, out, B, L, L, nh)    # as the forward runs it
     torch.cuda.synchronize()
     x = torch.randn((M, D), generator=g, device="cuda")
     tab = torch.zeros((6, D), device="cuda")
