@@ -132,6 +132,17 @@ wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void* k, int64_
  * negative or nh <= 0). */
 int64_t wan_op_attention_workspace_bytes(int64_t B, int64_t Lq, int32_t nh);
 
+/* wan_op_attention_ws without a caller workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the workspace is a
+ * static device array of the library, 8.8 MB on each GPU it runs on, held until the process ends.  Limits:
+ * at most 16384 (batch, head, 256-query) units per call (B * nh * ceil(Lq / 256)), and a key-split last
+ * round of at most 64 workgroups (otherwise the same softmax and merge as wan_op_attention_ws).  Larger
+ * calls fail with WAN_ERR_UNSUPPORTED before any launch.  Allocates nothing.  Every call on a GPU uses that
+ * GPU's one array: calls that overlap in time on one GPU (two streams, two threads) race.  Nothing in the
+ * array needs clearing between calls (every value read is written earlier in the same call). */
+wan_status wan_op_attention_noalloc(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt, int64_t ldv,
+                                    void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int32_t nh, void* stream);
+
 /* Timestep embedding, fp32 throughout (WanAnimate page, configuration section: freq_dim 256, the
  * time embedder kept in fp32; WanPipeline notes: temb (B, D), timestep_proj (B, 6D)):
  *   s = [cos(t w_i), sin(t w_i)], w_i = 10000^(-i/(freq_dim/2))

@@ -85,6 +85,8 @@ _op_transpose_v = _sig("wan_op_transpose_v", [_vp, _i64, _i64, _i64, _i64, _i32,
 _op_attention = _sig("wan_op_attention", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp])
 _op_attention_ws = _sig("wan_op_attention_ws", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i32, _vp,
                                                 _i64, _vp])
+_op_attention_noalloc = _sig("wan_op_attention_noalloc", [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64,
+                                                          _i32, _vp])
 _op_attention_ws_bytes = _sig("wan_op_attention_workspace_bytes", [_i64, _i64, _i32], C.c_int64)
 _op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
 _probe_mfma = _sig("wan_probe_mfma", [_vp, _i32, _i64, _i32, _vp])
@@ -93,7 +95,7 @@ EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_forward_image", "wan_d
             "wan_dit_time_attention", "wan_dit_attention_time",
             "wan_op_patchify", "wan_op_unpatchify", "wan_op_cfg_euler", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
-            "wan_op_attention_ws", "wan_op_attention_workspace_bytes",
+            "wan_op_attention_ws", "wan_op_attention_workspace_bytes", "wan_op_attention_noalloc",
             "wan_op_time_embed", "wan_probe_mfma"]
 
 
@@ -333,6 +335,14 @@ def op_attention_ws(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: tor
     _check(_op_attention_ws(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(), vt.shape[3],
                             out.data_ptr(), out.stride(0), b, lq, lkv, nh, workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def op_attention_noalloc(q: torch.Tensor, k: torch.Tensor, vt: torch.Tensor, out: torch.Tensor, b: int, lq: int, lkv: int,
+                         nh: int, stream=None):
+    """op_attention_ws with the library's static workspace (wan_op_attention_noalloc: allocates nothing)."""
+    _check(_op_attention_noalloc(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0), vt.data_ptr(), vt.shape[3],
+                                 out.data_ptr(), out.stride(0), b, lq, lkv, nh, _stream(stream)))
     return out
 
 

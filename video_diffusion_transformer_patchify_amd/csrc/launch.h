@@ -55,5 +55,13 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
                             bool accumulate = false, int64_t split_cap = 256);
 // split_cap: most workgroups a key-split last round may use (the workspace holds their partial results)
 int64_t attention_workspace_bytes(int64_t B, int64_t Lq, int nh, int64_t split_cap = 256);
+// launch_attention with a workspace in the library's static device array (no allocation): at most
+// attention_scratch_max_units() (batch, head, 256-query) units per call, a key split of at most 64
+// workgroups; calls that overlap on one GPU share the array and race
+hipError_t launch_attention_noalloc(const bf16_t* q, int64_t ldq, const bf16_t* k, int64_t ldk, const bf16_t* vt,
+                                    int64_t ldv, bf16_t* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv, int nh,
+                                    hipStream_t s);
+int64_t attention_scratch_max_units();
+int64_t attention_scratch_bytes();
 
 hipError_t launch_mfma_probe(float* sink, int blocks, int64_t rounds, int random_operands, hipStream_t s);

@@ -930,6 +930,25 @@ extern "C" wan_status wan_op_attention_ws(const void* q, int64_t ldq, const void
   return WAN_OK;
 }
 
+extern "C" wan_status wan_op_attention_noalloc(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* vt,
+                                                int64_t ldv, void* o, int64_t ldo, int64_t B, int64_t Lq, int64_t Lkv,
+                                                int32_t nh, void* stream) {
+  g_err.clear();
+  REQUIRE(B >= 0 && Lq >= 0 && nh > 0, WAN_ERR_SHAPE, "attention: bad sizes");
+  REQUIRE(Lkv >= 1 || B * Lq == 0, WAN_ERR_SHAPE, "attention: at least one key is needed");
+  REQUIRE(ldv % 64 == 0 && ldv >= Lkv, WAN_ERR_SHAPE, "attention: ldv must be a multiple of 64 and >= Lkv");
+  REQUIRE(ldq % 8 == 0 && ldk % 8 == 0 && ldo % 4 == 0 && ldq >= 128LL * nh && ldk >= 128LL * nh && ldo >= 128LL * nh,
+          WAN_ERR_SHAPE, "attention: bad row strides");
+  REQUIRE((q && k && vt && o) || B * Lq == 0, WAN_ERR_INVALID_ARG, "attention: NULL pointer");
+  const int64_t units = B * nh * ceil_div(Lq, 256);
+  REQUIRE(units <= attention_scratch_max_units(), WAN_ERR_UNSUPPORTED,
+          "attention_noalloc: %lld (batch, head, 256-query) units exceed the static workspace's %lld",
+          (long long)units, (long long)attention_scratch_max_units());
+  HIP_TRY(launch_attention_noalloc((const bf16_t*)q, ldq, (const bf16_t*)k, ldk, (const bf16_t*)vt, ldv, (bf16_t*)o, ldo, B,
+                                   Lq, Lkv, nh, (hipStream_t)stream), "attention_noalloc");
+  return WAN_OK;
+}
+
 extern "C" wan_status wan_op_time_embed(const float* t, int64_t rows, int32_t freq_dim, int64_t D, const float* w1,
                                         const float* b1, const float* w2, const float* b2, const float* wp, const float* bp,
                                         float* temb, float* tproj, float* work, void* stream) {
