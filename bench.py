@@ -235,6 +235,134 @@ def vendor_reference(cfg):
     print(json.dumps({"vendor_reference": res, "workload": cfg.name}), flush=True)
 
 
+def vae_cpu_baseline(cfg, crop=(20, 26), frames=2):
+    """fp64 oracle on a bounded sample of the decoder workload: the first `frames` latent frames of the
+    workload's seeded latent, cropped to `crop` latent pixels, decoded whole; the decoder's work is
+    convolutions of uniform cost per FLOP, so the full decode is estimated as its FLOPs at the sample's
+    FLOP rate."""
+    from oracle import wan_vae_oracle as V
+    from wan_inputs.vae import VaeWeights, decoder_layout, draw_vae_latent
+
+    threads = len(os.sched_getaffinity(0))
+    w = VaeWeights(cfg)
+    P = V.weights_f64(w)
+    z = draw_vae_latent(cfg, frames=frames).f64()[0][:, :, :crop[0], :crop[1]]
+    t0 = time.perf_counter()
+    V.decode_whole(z, P, decoder_layout(cfg), cfg.eps)
+    t = time.perf_counter() - t0
+    fl = V.decoder_flops(frames, crop[0], crop[1], decoder_layout(cfg))
+    return fl / t, t, threads
+
+
+def vae_probe(cfg):
+    """One launch each of the decoder kernels whose counters rocprofv3 reads, at the workload's stage-D
+    shapes (96 channels, 8H x 8W, 16 frames: one chunk of 4 latent frames), plus the 1 GiB calibration copy."""
+    import torch
+
+    from video_diffusion_transformer_patchify_amd import binding as Bd
+
+    torch.cuda.set_device(0)
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    C, H, W, nf = cfg.base_dim, 8 * cfg.height, 8 * cfg.width, 16
+    g = torch.Generator(device="cuda").manual_seed(0)
+
+    def frame():
+        f = torch.zeros(((C + 15) // 16, H + 2, W + 2, 16), dtype=torch.bfloat16, device="cuda")
+        f[:, 1:-1, 1:-1] = torch.randn((f.shape[0], H, W, 16), generator=g, device="cuda").to(torch.bfloat16)
+        return f
+
+    xs = [frame() for _ in range(nf + 2)]
+    outs = [torch.zeros_like(xs[0]) for _ in range(nf)]
+    w = (torch.randn((C, C, 3, 3, 3), generator=g, device="cuda") / (27 * C) ** 0.5).to(torch.bfloat16)
+    wp = Bd.op_vae_pack_conv(w)
+    b = torch.zeros(C, device="cuda")
+    ins = [xs[j + dt] for j in range(nf) for dt in range(3)]
+    torch.cuda.synchronize()
+    Bd.op_vae_conv(ins, 3, 3, 0, wp, b, C, C, 1, H, W, outs)
+    torch.cuda.synchronize()
+    gam = torch.ones(C, device="cuda")
+    Bd.op_vae_rms_silu(xs[:nf], outs, C, H, W, gam, 1e-6)
+    torch.cuda.synchronize()
+    print("vae probe done", flush=True)
+
+
+def bench_vae(args):
+    """A step is one wan_vae_decode of the whole latent (all latent frames, per-frame feature caches),
+    inputs resident in HBM; value = the decoder's algorithmic convolution FLOPs per second."""
+    import torch
+
+    from oracle import wan_vae_oracle as V  # noqa: F401  (FLOP count only)
+    from video_diffusion_transformer_patchify_amd import binding as Bd
+    from video_diffusion_transformer_patchify_amd.harness import to_device, upload_weights
+    from wan_inputs.vae import VaeWeights, decoder_layout, draw_vae_latent, get_vae_config
+
+    cfg = get_vae_config(args.vae_config)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    model = Bd.WanVAE(Bd.make_vae_config(cfg, chunk_frames=args.chunk_frames), upload_weights(VaeWeights(cfg)),
+                      stream=stream)
+    lat = to_device(draw_vae_latent(cfg))
+    video = torch.empty(cfg.out_shape, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    print(f"# device bytes {model.device_bytes / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        model.decode(lat, video, stream=stream)
+    torch.cuda.synchronize()
+    model.time_convs(4096)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        model.decode(lat, video, stream=stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    conv_ms, conv_n, conv_fl = model.conv_time()
+    model.time_convs(0)
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    assert torch.isfinite(video.float()).all().item(), "non-finite video"
+    fl = V.decoder_flops(cfg.frames, cfg.height, cfg.width, decoder_layout(cfg))
+    tflops = fl / (ms * 1e-3) / 1e12
+    conv_tf = conv_fl / (conv_ms * 1e-3) / 1e12
+    print(f"# {ms:.2f} ms/decode = {tflops:.1f} TFLOP/s; 3x3x3 convs {conv_n} launches {conv_ms / conv_n:.3f} ms avg, "
+          f"{conv_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    res = {
+        "metric": f"Wan-VAE decode TFLOP/s, latent {list(cfg.latent_shape)} -> video {list(cfg.out_shape)}, bf16",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "ms_per_step_median": round(per_step[len(per_step) // 2], 3),
+        "video_frames_per_s": round(cfg.out_frames * cfg.batch / (ms * 1e-3), 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latent, N(0, 1/fan_in) random-init conv weights)",
+        "config": {"workload": f"{cfg.name}: Wan2.1 VAE decoder (widths {list(cfg.dims)}), latent {list(cfg.latent_shape)}, "
+                               f"chunks of {args.chunk_frames} latent frames after the first",
+                   "global_batch": cfg.batch, "seq_len": cfg.out_frames, "parallelism": "single GPU"},
+        "flops_per_step": fl,
+        "mfma_frac_end_to_end": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "k_vae_conv<3,3,0,3> (3x3x3 causal convs with 96-channel tiles: conv_in and the "
+                               "residual-block convs)", "bound": "mfma", "achieved": round(conv_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(conv_tf / PEAK_BF16_TFLOPS, 4),
+                     "ms_per_launch": round(conv_ms / conv_n, 4), "flops_per_launch": round(conv_fl / conv_n),
+                     "launches_timed": conv_n, "timed_where": "inside the timed decodes",
+                     "traffic": traffic_for("k_vae.hip")},
+    }
+    model.close()
+    del video, lat
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        rate, t, threads = vae_cpu_baseline(cfg)
+        res["cpu_baseline"] = {
+            "value": round(rate / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "ms_per_step": round(fl / rate * 1e3, 1),
+            "sample": f"fp64 numpy oracle decoding the workload's first 2 seeded latent frames cropped to 20 x 26 "
+                      f"latent pixels ({t:.1f}s); the full decode estimated as its FLOPs at that rate",
+        }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,10 +374,22 @@ def main():
     ap.add_argument("--probe", action="store_true", help="run the counter-calibration kernels only (for rocprofv3 --pmc)")
     ap.add_argument("--vendor-reference", action="store_true",
                     help="time hipBLASLt GEMMs and torch SDPA next to this library's kernels on the workload's shapes")
+    ap.add_argument("--workload", choices=("dit", "vae"), default="dit",
+                    help="dit: the DiT forward (default); vae: the Wan-VAE causal decoder")
+    ap.add_argument("--vae-config", type=int, default=14, help="decoder workload id (11..15); 14 = 81 x 480 x 832")
+    ap.add_argument("--chunk-frames", type=int, default=4, help="decoder: latent frames per chunk after the first")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
+    if args.workload == "vae":
+        if args.probe:
+            from wan_inputs.vae import get_vae_config
+
+            vae_probe(get_vae_config(args.vae_config))
+        else:
+            bench_vae(args)
+        return
     if args.probe or args.vendor_reference:
         from wan_inputs import get_config
 

@@ -26,7 +26,7 @@ def built_library():
 
 def declared_functions():
     names = []
-    for h in ("wan_dit.h", "wan_ops.h"):
+    for h in ("wan_dit.h", "wan_ops.h", "wan_vae.h"):
         text = open(os.path.join(ROOT, "include", h)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         names += re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(wan_\w+)\s*\(", text, flags=re.M)
@@ -84,3 +84,32 @@ def test_validation_errors_without_gpu():
                            None) == 1                                                           # gate missing
     assert B._op_qk_norm_rope(1, 4608, 4, 1536, 1e-6, 0, 1, 1536, 1, 1, 10, 2, 2, 2, 44, 42, 42, 1.0, None) == 2
     assert B._op_rope_table(1, 5, 8, 8, 44, 42, 40, 1e4, None) == 2                              # dims sum != 128
+
+
+def test_vae_validation_errors_without_gpu():
+    from video_diffusion_transformer_patchify_amd import binding as B
+    from wan_inputs.vae import get_vae_config
+
+    h = C.c_void_p()
+    assert B._vae_create(None, None, 0, None, C.byref(h)) == 1
+    c = B.make_vae_config(get_vae_config(14))
+    c.z_dim = 48
+    assert B._vae_create(C.byref(c), None, 0, None, C.byref(h)) == 4
+    c = B.make_vae_config(get_vae_config(14), chunk_frames=5)
+    assert B._vae_create(C.byref(c), None, 0, None, C.byref(h)) == 1
+    assert "chunk_frames" in B._vae_last_error().decode()
+    c = B.make_vae_config(get_vae_config(14))
+    assert B._vae_create(C.byref(c), None, 0, None, C.byref(h)) == 7
+    assert "latents_mean" in B._vae_last_error().decode()
+    assert B._vae_decode(None, None, None, None) == 1
+    assert B._vae_op_packed_elems(96, 96, 2, 3) == -1
+    assert B._vae_op_packed_elems(96, 96, 3, 3) == 96 * 3 * 6 * 9 * 16
+    assert B._vae_op_packed_elems(3, 96, 3, 3) == 32 * 3 * 6 * 9 * 16
+    one = (C.c_void_p * 3)(1, 1, 1)
+    outs = (C.c_void_p * 2)(1, 1)
+    assert B._vae_op_conv(one, 3, 3, 0, 1, 1, 24, 96, 1, 8, 8, outs, None, 1, None) == 2        # c_in % 16
+    assert B._vae_op_conv(one, 3, 3, 1, 1, 1, 96, 96, 1, 8, 8, outs, None, 1, None) == 1        # up needs kt 1
+    assert B._vae_op_conv(one, 3, 3, 0, 1, 1, 96, 96, 2, 8, 8, outs, None, 1, None) == 4        # split: time conv
+    assert B._vae_op_conv(one, 1, 3, 1, 1, 1, 96, 96, 1, 7, 8, outs, None, 1, None) == 2        # odd H with up
+    assert B._vae_op_conv(one, 3, 3, 0, 1, 1, 96, 96, 1, 8, 8, outs, None, 17, None) == 1       # nf
+    assert B._vae_op_rms_silu(one, one, 1, 96, 8, 8, 1, 1e-6, None) == 1                        # aliasing

@@ -353,3 +353,24 @@ def test_decoder_flop_count_by_brute_force():
         for wn, t_, h_, w_ in convs:
             total += 2 * int(np.prod(spec[wn])) * t_ * h_ * w_
     assert V.decoder_flops(cfg.frames, cfg.height, cfg.width, decoder_layout(cfg)) == total
+
+
+def test_decoder_goldens_come_from_the_current_oracle():
+    """tests/golden/vae_cfg*_first2.npz were written by this oracle (or one listed as arithmetic-equivalent),
+    and their sample positions lie inside the first five frames of the workload's video."""
+    import hashlib
+
+    hashes = json.load(open(os.path.join(HERE, "golden", "oracle_hashes.json")))["vae"]
+    src = hashlib.sha256(open(os.path.join(os.path.dirname(HERE), "oracle", "wan_vae_oracle.py"), "rb").read())
+    assert hashes["current"] == src.hexdigest()[:16]
+    ok = {hashes["current"], *hashes["equivalent"]}
+    for cfg_id in (13, 14):
+        g = np.load(os.path.join(HERE, "golden", f"vae_cfg{cfg_id}_first2.npz"))
+        assert str(g["oracle"][0]) in ok
+        cfg = get_vae_config(cfg_id)
+        assert int(g["frames"][0]) == 5
+        pos = g["positions"]
+        hi = np.array([3, 5, cfg.out_shape[3], cfg.out_shape[4]])
+        assert pos.min() >= 0 and np.all(pos.max(axis=0) < hi) and len(pos) > 30000
+        assert len(np.unique(pos, axis=0)) == len(pos)
+        assert np.all(np.abs(g["values"]) <= 1.0) and 0.3 < float(g["video_std"][0]) < 0.8

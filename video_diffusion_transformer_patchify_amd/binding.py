@@ -1,4 +1,4 @@
-"""ctypes binding of libwan_dit.so (include/wan_dit.h, include/wan_ops.h).
+"""ctypes binding of libwan_dit.so (include/wan_dit.h, include/wan_ops.h, include/wan_vae.h).
 
 Argument marshalling only: every stage runs in the HIP library.  torch provides device memory and the
 current stream.  If the library has not been built this module raises at import time; there is no
@@ -91,12 +91,34 @@ _op_attention_ws_bytes = _sig("wan_op_attention_workspace_bytes", [_i64, _i64, _
 _op_time_embed = _sig("wan_op_time_embed", [_vp, _i64, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
 _probe_mfma = _sig("wan_probe_mfma", [_vp, _i32, _i64, _i32, _vp])
 
+
+class WanVaeConfig(C.Structure):
+    _fields_ = [("z_dim", C.c_int32), ("base_dim", C.c_int32), ("chunk_frames", C.c_int32), ("eps", C.c_float),
+                ("max_height", C.c_int64), ("max_width", C.c_int64), ("reserved", C.c_int64 * 2)]
+
+
+_vae_create = _sig("wan_vae_create", [C.POINTER(WanVaeConfig), C.POINTER(WanWeight), C.c_size_t, _vp, C.POINTER(_vp)])
+_vae_decode = _sig("wan_vae_decode", [_vp, C.POINTER(WanTensor), C.POINTER(WanTensor), _vp])
+_vae_destroy = _sig("wan_vae_destroy", [_vp], None)
+_vae_last_error = _sig("wan_vae_last_error", [], C.c_char_p)
+_vae_device_bytes = _sig("wan_vae_device_bytes", [_vp], _i64)
+_vae_time_convs = _sig("wan_vae_time_convs", [_vp, _i64])
+_vae_conv_time = _sig("wan_vae_conv_time", [_vp, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)])
+_vae_op_packed_elems = _sig("wan_vae_op_packed_conv_elems", [_i64, _i64, _i32, _i32], _i64)
+_vae_op_pack_conv = _sig("wan_vae_op_pack_conv", [_vp, _i32, _i64, _i64, _i32, _i32, _vp, _vp])
+_vae_op_conv = _sig("wan_vae_op_conv", [C.POINTER(_vp), _i32, _i32, _i32, _vp, _vp, _i64, _i64, _i32, _i64, _i64,
+                                        C.POINTER(_vp), C.POINTER(_vp), _i32, _vp])
+_vae_op_rms_silu = _sig("wan_vae_op_rms_silu", [C.POINTER(_vp), C.POINTER(_vp), _i32, _i64, _i64, _i64, _vp, _f32, _vp])
+
 EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_forward_image", "wan_dit_denoise_step", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
             "wan_dit_time_attention", "wan_dit_attention_time",
             "wan_op_patchify", "wan_op_unpatchify", "wan_op_cfg_euler", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
             "wan_op_attention_ws", "wan_op_attention_workspace_bytes", "wan_op_attention_noalloc",
-            "wan_op_time_embed", "wan_probe_mfma"]
+            "wan_op_time_embed", "wan_probe_mfma",
+            "wan_vae_create", "wan_vae_decode", "wan_vae_destroy", "wan_vae_last_error", "wan_vae_device_bytes",
+            "wan_vae_time_convs", "wan_vae_conv_time",
+            "wan_vae_op_packed_conv_elems", "wan_vae_op_pack_conv", "wan_vae_op_conv", "wan_vae_op_rms_silu"]
 
 
 def last_error() -> str:
@@ -106,6 +128,11 @@ def last_error() -> str:
 def _check(status: int):
     if status != 0:
         raise WanError(status, last_error())
+
+
+def _check_vae(status: int):
+    if status != 0:
+        raise WanError(status, (_vae_last_error() or b"").decode())
 
 
 def _stream(stream=None) -> int:
@@ -157,28 +184,33 @@ def make_config(cfg, max_batch=None, max_tokens=None, max_text_len=None, num_lay
     return c
 
 
+def _weight_array(weights: dict):
+    names = list(weights)
+    arr = (WanWeight * len(names))()
+    keep = []
+    for i, n in enumerate(names):
+        t = weights[n]
+        if not t.is_cuda or not t.is_contiguous():
+            raise WanError(1, f"weight {n} must be a contiguous device tensor")
+        b = n.encode()
+        keep.append(b)
+        arr[i].name = b
+        arr[i].data = t.data_ptr()
+        arr[i].dtype = _dtype_code(t)
+        arr[i].ndim = t.dim()
+        for j, s in enumerate(t.shape):
+            arr[i].shape[j] = s
+    return arr, keep
+
+
 class WanDiT:
     """Handle around wan_dit_create / wan_dit_forward / wan_dit_destroy."""
 
     def __init__(self, config: WanDitConfig, weights: dict, stream=None):
-        names = list(weights)
-        arr = (WanWeight * len(names))()
-        self._keep = []
-        for i, n in enumerate(names):
-            t = weights[n]
-            if not t.is_cuda or not t.is_contiguous():
-                raise WanError(1, f"weight {n} must be a contiguous device tensor")
-            b = n.encode()
-            self._keep.append(b)
-            arr[i].name = b
-            arr[i].data = t.data_ptr()
-            arr[i].dtype = _dtype_code(t)
-            arr[i].ndim = t.dim()
-            for j, s in enumerate(t.shape):
-                arr[i].shape[j] = s
+        arr, self._keep = _weight_array(weights)
         self.config = config
         h = C.c_void_p()
-        _check(_create(C.byref(config), arr, len(names), _stream(stream), C.byref(h)))
+        _check(_create(C.byref(config), arr, len(arr), _stream(stream), C.byref(h)))
         self._h = h
 
     @property
@@ -373,3 +405,100 @@ def probe_mfma(blocks: int = 1024, rounds: int = 1000, random_operands: bool = T
         if i:
             best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     return best
+
+
+# ------------------------------------------------------------------------------------------------
+# Wan-VAE causal decoder (include/wan_vae.h)
+# ------------------------------------------------------------------------------------------------
+
+
+def make_vae_config(cfg, chunk_frames: int = 4, max_height: int = None, max_width: int = None) -> WanVaeConfig:
+    """Fill the C config from a wan_inputs.vae.VaeConfig."""
+    c = WanVaeConfig()
+    c.z_dim, c.base_dim, c.chunk_frames, c.eps = cfg.z_dim, cfg.base_dim, chunk_frames, cfg.eps
+    c.max_height = max_height or cfg.height
+    c.max_width = max_width or cfg.width
+    return c
+
+
+class WanVAE:
+    """Handle around wan_vae_create / wan_vae_decode / wan_vae_destroy."""
+
+    def __init__(self, config: WanVaeConfig, weights: dict, stream=None):
+        arr, self._keep = _weight_array(weights)
+        self.config = config
+        h = C.c_void_p()
+        _check_vae(_vae_create(C.byref(config), arr, len(arr), _stream(stream), C.byref(h)))
+        self._h = h
+
+    @property
+    def device_bytes(self) -> int:
+        return int(_vae_device_bytes(self._h))
+
+    def decode(self, latent: torch.Tensor, video: torch.Tensor = None, dtype=None, stream=None) -> torch.Tensor:
+        """latent [B, 16, F, H, W] -> video [B, 3, 1 + 4 (F - 1), 8H, 8W] (latent's dtype unless given)."""
+        if video is None:
+            b, _, f, h, w = latent.shape
+            video = torch.empty((b, 3, 1 + 4 * (f - 1), 8 * h, 8 * w), dtype=dtype or latent.dtype, device=latent.device)
+        lt, vt = as_wan_tensor(latent), as_wan_tensor(video)
+        _check_vae(_vae_decode(self._h, C.byref(lt), C.byref(vt), _stream(stream)))
+        return video
+
+    def time_convs(self, max_launches: int):
+        """Bracket the next `max_launches` 3x3x3 convolution launches (96-channel tiles) of decode() with HIP
+        events (0: off)."""
+        _check_vae(_vae_time_convs(self._h, int(max_launches)))
+
+    def conv_time(self):
+        """(total ms, launches, algorithmic FLOPs) of the convolution launches timed since the last call."""
+        ms, n, fl = C.c_double(), C.c_int64(), C.c_double()
+        _check_vae(_vae_conv_time(self._h, C.byref(ms), C.byref(n), C.byref(fl)))
+        return ms.value, int(n.value), fl.value
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _vae_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def vae_packed_conv_elems(c_out: int, c_in: int, kt: int, ks: int) -> int:
+    return int(_vae_op_packed_elems(c_out, c_in, kt, ks))
+
+
+def op_vae_pack_conv(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """Conv weight [c_out, c_in, kt, ks, ks] (or [c_out, c_in, ks, ks]) -> packed bf16 device tensor."""
+    if w.dim() == 4:
+        w = w[:, :, None]
+    co, ci, kt, ks, _ = w.shape
+    out = torch.empty(vae_packed_conv_elems(co, ci, kt, ks), dtype=torch.bfloat16, device=w.device)
+    _check_vae(_vae_op_pack_conv(w.contiguous().data_ptr(), _dtype_code(w), co, ci, kt, ks, out.data_ptr(),
+                                 _stream(stream)))
+    return out
+
+
+def _ptrs(ts):
+    arr = (_vp * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def op_vae_conv(inputs, kt: int, ks: int, up: int, w_packed: torch.Tensor, bias: torch.Tensor, c_in: int, c_out: int,
+                split: int, H: int, W: int, outputs, residuals=None, stream=None):
+    """wan_vae_op_conv on padded frames: inputs [nf * kt] frame tensors (in[j * kt + dt]), outputs
+    [nf * split], residuals None or [nf * split] (entries may be None)."""
+    nf = len(outputs) // split
+    res = _ptrs(residuals) if residuals is not None else None
+    _check_vae(_vae_op_conv(_ptrs(inputs), kt, ks, up, w_packed.data_ptr(), bias.data_ptr(), c_in, c_out, split, H, W,
+                            _ptrs(outputs), res, nf, _stream(stream)))
+
+
+def op_vae_rms_silu(inputs, outputs, c: int, H: int, W: int, gamma: torch.Tensor, eps: float, stream=None):
+    _check_vae(_vae_op_rms_silu(_ptrs(inputs), _ptrs(outputs), len(inputs), c, H, W, gamma.data_ptr(), eps,
+                                _stream(stream)))
