@@ -347,7 +347,9 @@ def bench_vae(args):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(conv_tf / PEAK_BF16_TFLOPS, 4),
                      "ms_per_launch": round(conv_ms / conv_n, 4), "flops_per_launch": round(conv_fl / conv_n),
                      "launches_timed": conv_n, "timed_where": "inside the timed decodes",
-                     "traffic": traffic_for("k_vae.hip")},
+                     "traffic": traffic_for("k_vae.hip"),
+                     "traffic_shape": "one stage-D launch (96 -> 96 channels, 16 frames of 480 x 832), "
+                                      "rocprofv3 FETCH_SIZE / WRITE_SIZE of bench.py --workload vae --probe"},
     }
     model.close()
     del video, lat
