@@ -502,6 +502,209 @@ __global__ __launch_bounds__(256) void k_attn_combine(AttnArgs a) {
   *op = (bf16_t)(pack_bf16x2(acc / l + prev, 0.f) & 0xFFFFu);
 }
 
+// ---------------------------------------------------------------------------------------------------
+// Cross-attention with the whole key set resident in LDS (at most RES_TILES * 64 keys: the text context).
+// Persistent: one workgroup per CU walks a contiguous range of (batch, head, 256-query) units, loading a
+// head's K and Vt tiles once (they stay for every query tile of that head it owns); each unit's Q is read
+// into registers while the previous unit stores, and its output leaves through LDS as whole rows, so a
+// unit costs its MFMA work and little else.  The probabilities are offset-free as in k_flash_attn, with
+// the same redo marks: a wave whose rows leave the safe range stores nothing and marks its unit, and the
+// exact k_flash_attn launched after it recomputes the marked units.
+// ---------------------------------------------------------------------------------------------------
+constexpr int RES_TILES = 4;
+
+// One pass over the resident sub-tiles for the wave's two query blocks, software pipelined as in
+// k_flash_attn (the scores of sub-tile j + 1 are formed with the probabilities of sub-tile j).
+template <bool EXACT>
+__device__ __forceinline__ void resident_pass(AttnState& st, const u32x4 (&qf)[2][8], char (*lds)[TILE_BYTES],
+                                              int n_sub, int last_lim, int l32, int g) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.o[qb][i] = (f32x16){};
+    st.m[qb] = 0.f;
+    st.l_run[qb] = 0.f;
+  }
+  st.bad = false;
+  f32x16 s_cur[2], s_next[2];
+  scores(s_next, qf, lds[0], 0, l32, g);
+  if (n_sub == 1 && last_lim < KS) mask_scores(s_next, g, last_lim);
+  to_vgprs(s_next, s_cur);
+  {
+    const float mx0 = row_max(s_cur[0]), mx1 = row_max(s_cur[1]);
+    if constexpr (EXACT) {
+      st.m[0] = mx0;
+      st.m[1] = mx1;
+    } else {
+      st.bad = __any(!(fminf(mx0, mx1) >= MAX_FLOOR));
+    }
+  }
+  int j = 0;
+  for (; j + 2 < n_sub; ++j) {
+    u32x4 pf[2][2];
+    scores(s_next, qf, lds[(j + 1) >> 1], (j + 1) & 1, l32, g);
+    softmax_step<EXACT>(st, s_cur, pf);
+    pv(st, pf, lds[j >> 1] + K_TILE_BYTES, j & 1, l32, g);
+    to_vgprs(s_next, s_cur);
+  }
+  if (j + 1 < n_sub) {
+    u32x4 pf[2][2];
+    scores(s_next, qf, lds[(j + 1) >> 1], (j + 1) & 1, l32, g);
+    if (last_lim < KS) mask_scores(s_next, g, last_lim);
+    softmax_step<EXACT>(st, s_cur, pf);
+    pv(st, pf, lds[j >> 1] + K_TILE_BYTES, j & 1, l32, g);
+    to_vgprs(s_next, s_cur);
+    ++j;
+  }
+  {
+    u32x4 pf[2][2];
+    softmax_step<EXACT>(st, s_cur, pf);
+    pv(st, pf, lds[j >> 1] + K_TILE_BYTES, j & 1, l32, g);
+  }
+}
+
+constexpr int OSTAGE_BYTES = 32 * 256;   // one wave's 32 output rows of 128 bf16
+
+__global__ __launch_bounds__(256, 1) void k_cross_attn(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char lds[RES_TILES][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ostage[4][OSTAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int64_t nwg = gridDim.x;
+  const int u0 = (int)((int64_t)blockIdx.x * a.units / nwg), u1 = (int)((int64_t)(blockIdx.x + 1) * a.units / nwg);
+  const int64_t Lkv = a.Lkv;
+  const int n_tiles = (int)((Lkv + KT - 1) / KT);
+  const int n_sub = (int)((Lkv + KS - 1) / KS);
+  const int last_lim = (int)(Lkv - (int64_t)(n_sub - 1) * KS);
+  // per-lane offsets of the direct loads, as in k_flash_attn
+  uint32_t k_off[4], v_off[4];
+  int k_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int I = 4 * wave + i;
+    k_row[i] = 4 * I + (lane >> 4);
+    const int k_col = ((lane & 15) ^ k_swz(k_row[i])) * 8;
+    k_off[i] = (uint32_t)(((int64_t)k_row[i] * a.ldk + k_col) * 2);
+    const int v_row = 8 * I + (lane >> 3);
+    const int v_col = ((lane & 7) ^ v_swz(v_row)) * 8;
+    v_off[i] = (uint32_t)(((int64_t)v_row * a.ldv + v_col) * 2);
+  }
+  const bool scale_q = a.q_mul != 1.0f;
+  // Q of a unit (query l32 of block qb, d = 16 s + 8 g .. +7), read into registers.  The next unit's Q is
+  // requested right after this unit's MFMAs and before its stores (the stores are unconditional, so the
+  // wait for it at the next unit counts them and does not wait for them).
+  const int qrow0 = wave * QWAVE + l32;
+  u32x4 nq[2][8];
+  auto load_q = [&](int u) {
+    const int qt = u % a.q_tiles, bh = u / a.q_tiles;
+    const int h = bh % a.nh, b = bh / a.nh;
+    const char* qbase = (const char*)(a.q + ((int64_t)b * a.Lq + (int64_t)qt * QB) * a.ldq + h * 128);
+    const int lim = (int)(a.Lq - 1 - (int64_t)qt * QB);   // rows past Lq re-read the last row
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r = min(qrow0 + 32 * qb, lim);
+      const uint32_t off = (uint32_t)((r * (int)a.ldq + g * 8) * 2);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) nq[qb][s] = *(const u32x4*)(qbase + off + 32 * s);
+    }
+  };
+  if (u0 < u1) load_q(u0);
+  int cur_bh = -1;
+  for (int u = u0; u < u1; ++u) {
+    const int qt = u % a.q_tiles, bh = u / a.q_tiles;
+    const int h = bh % a.nh, b = bh / a.nh;
+    if (bh != cur_bh) {
+      // a new head: every wave is past its reads of the previous one, then its K and Vt tiles come in
+      block_sync();
+      const bf16_t* kbase = a.k + (int64_t)b * a.Lkv * a.ldk + h * 128;
+      const bf16_t* vbase = a.vt + ((int64_t)b * a.nh + h) * 128 * a.ldv;
+      for (int t = 0; t < n_tiles; ++t) {
+        const int64_t key0 = (int64_t)t * KT;
+        const char* kt = (const char*)(kbase + key0 * a.ldk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // rows past the last key re-read the last valid one (their scores are masked)
+          const int64_t key = key0 + k_row[i] < Lkv ? k_row[i] : Lkv - 1 - key0;
+          const uint32_t off = (uint32_t)(k_off[i] + (key - k_row[i]) * a.ldk * 2);
+          __builtin_amdgcn_global_load_lds((const void*)(kt + off), (lds_void*)(lds[t] + (4 * wave + i) * 1024), 16,
+                                           0, 0);
+        }
+        const char* vtb = (const char*)(vbase + key0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(vtb + v_off[i]),
+                                           (lds_void*)(lds[t] + K_TILE_BYTES + (4 * wave + i) * 1024), 16, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+      block_sync();
+      cur_bh = bh;
+    }
+    u32x4 qf[2][8];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        u32x4 v = nq[qb][s];
+        if (scale_q) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(lo_bf16(v[e]) * a.q_mul, hi_bf16(v[e]) * a.q_mul);
+        }
+        asm volatile("; q fragment %0" : "=a"(qf[qb][s]) : "0"(v));
+      }
+    }
+    AttnState st;
+    resident_pass<false>(st, qf, lds, n_sub, last_lim, l32, g);
+    if (u + 1 < u1) load_q(u + 1);
+    // a wave whose rows left the offset-free range marks its unit for the exact kernel and stores nothing
+    if (lane == 0) a.flags[4 * (int64_t)u + wave] = st.bad ? 1u : 0u;
+    if (st.bad) continue;
+    // Normalise and store, one query block at a time through the wave's LDS stage: lane (l32, g) puts
+    // its 4-value runs of row l32 into 16-byte chunk c = 4 dt + rg (8-byte half g) at position c ^ (l32 &
+    // 15) (conflict-free), then 16 lanes per row read back the row's 16 chunks, so each store
+    // instruction writes 4 whole 256-byte rows.
+    char* stg = ostage[wave];
+    const int c16 = lane & 15, r4 = lane >> 4;
+    // a buffer resource covering this tile's valid rows: stores (and reads) of rows past Lq fall outside
+    // it and the hardware drops them, so every lane issues the same memory operations
+    const int64_t valid = a.Lq - (int64_t)qt * QB < QB ? a.Lq - (int64_t)qt * QB : QB;
+    const auto orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.o + ((int64_t)b * a.Lq + (int64_t)qt * QB) * a.ldo + h * 128), 0,
+        (int)((valid - 1) * a.ldo * 2 + 256), 0x00020000);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l_tot = st.l_run[qb] + __shfl_xor(st.l_run[qb], 32, 64);
+      const float inv = 1.0f / l_tot;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          u32x2 w;
+          w.x = pack_bf16x2(st.o[qb][dt][4 * rg] * inv, st.o[qb][dt][4 * rg + 1] * inv);
+          w.y = pack_bf16x2(st.o[qb][dt][4 * rg + 2] * inv, st.o[qb][dt][4 * rg + 3] * inv);
+          const int c = 4 * dt + rg;
+          *(u32x2*)(stg + l32 * 256 + ((c ^ (l32 & 15)) << 4) + 8 * g) = w;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the stage is written before any lane reads it
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 4 * i + r4;
+        u32x4 d = *(const u32x4*)(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
+        const int off = ((wave * QWAVE + qb * 32 + row) * (int)a.ldo + 8 * c16) * 2;
+        if (a.accumulate) {
+          const u32x4 prev = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(orsrc, off, 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            d[e] = pack_bf16x2(lo_bf16(d[e]) + lo_bf16(prev[e]), hi_bf16(d[e]) + hi_bf16(prev[e]));
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next block overwrites the stage
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 }  // namespace
 
 // Workspace: key-split partial outputs [split_cap][256][128] fp32, their (m, l) [split_cap][256][2], then the
@@ -536,6 +739,15 @@ hipError_t launch_attention(const bf16_t* q, int64_t ldq, const bf16_t* k, int64
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       n_cu <= 0)
     n_cu = 256;
+  if (!self_attn && Lkv <= RES_TILES * KT && ws != nullptr) {
+    // keys resident in LDS: the persistent cross-attention kernel, then the exact kernel on the units it
+    // marked (it returns at once for the others)
+    a.units = (int)units;
+    a.flags = (unsigned*)(ws + split_cap * QB * (128 + 2));
+    hipLaunchKernelGGL(k_cross_attn, dim3((unsigned)(units < n_cu ? units : n_cu)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_flash_attn<false, false, true>), dim3((unsigned)units), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int64_t tail = units % n_cu;
   int64_t split = 1, chunk = Lkv;
   if (ws != nullptr && tail > 0 && 2 * tail <= n_cu) {
