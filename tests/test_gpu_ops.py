@@ -344,6 +344,16 @@ def test_attention_key_split(G, B, Lq, Lkv, nh, fused):
     _attn_case(G, B, Lq, Lkv, nh, fused, f"ks{B}_{Lq}_{Lkv}_{nh}", split=True)
 
 
+def test_cross_attention_resident_many_units(G):
+    """More (batch, head, query-tile) units than CUs with the workspace path: the persistent cross kernel
+    (text keys resident in LDS) walks several units per workgroup across head changes, with a ragged
+    last query tile; sampled query rows of every batch element against the oracle."""
+    G.note("cross attention resident, many units")
+    rows = np.unique(np.concatenate([np.arange(0, 8200, 37), np.arange(8150, 8200)]))
+    _attn_case(G, 2, 8200, 226, 12, False, "xres", rows=rows, split=True)
+    _attn_case(G, 1, 2000, 256, 5, False, "xres256", split=True)
+
+
 def test_attention_key_split_peaked(G):
     """Scores in the tens with chunked keys: the merge rescales chunks whose running maxima differ."""
     G.note("attention key split peaked")
