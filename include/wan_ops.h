@@ -53,6 +53,23 @@ wan_status wan_op_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, c
                        int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
                        const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, void* stream);
 
+/* Size in bytes of wan_op_gemm_ws's workspace (fp32 partial tiles of at most one round of the
+ * persistent kernel: 256 tiles of 256 x 256). */
+int64_t wan_op_gemm_workspace_bytes(void);
+
+/* wan_op_gemm with a caller-owned device workspace (16-byte aligned, at least
+ * wan_op_gemm_workspace_bytes(); its contents on entry do not matter and are overwritten).  Same
+ * arguments, result and errors as wan_op_gemm, plus WAN_ERR_INVALID_ARG for a missing, misaligned or
+ * short workspace.  Where the persistent kernel's last round of 256 x 256 tiles would leave at least half
+ * of the CUs idle, that round's tiles are split along K (stream-K): each chunk writes an fp32 partial
+ * tile to the workspace and a fix-up pass adds them in chunk order, then the bias and the epilogue.
+ * The sums then differ from wan_op_gemm's by fp32 rounding order only.  Calls that share a workspace
+ * must be ordered (same stream). */
+wan_status wan_op_gemm_ws(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int64_t M, int64_t N,
+                          int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
+                          const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, void* workspace,
+                          int64_t workspace_bytes, void* stream);
+
 /* Residual add + LayerNorm over D (population variance, eps) of fp32 rows x [rows, D] -> bf16 y [rows, D]
  * (WanPipeline notes, WanTransformerBlock: hidden_states + attn_output * gate_msa, + attn_output,
  * + ff_output * c_gate_msa, each followed by the next norm).  With r = res [rows, D] bf16 and

@@ -153,6 +153,82 @@ def test_gemm_epilogues(G, M, N, K, epi):
     assert G.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max())
 
 
+# Stream-K tail (wan_op_gemm_ws): the persistent kernel's last round, when at most half full, runs split
+# along K.  (9000, 4104, 256): 36 x 17 = 612 tiles, 100 in the tail, 2 chunks of the minimum 4 K stages,
+# ragged M and N inside the tail tiles; (27280, 3072, 3072): the TI2V-5B output projections, 1284 tiles,
+# 4 in the tail, 24 chunks; (7920, 5120, 13824): the I2V stack's FFN2, 620 tiles, 108 in the tail, 2 chunks
+# of 216 stages.
+SK_CASES = [(9000, 4104, 256), (27280, 3072, 3072), (7920, 5120, 13824)]
+
+
+@pytest.mark.parametrize("M,N,K", SK_CASES)
+@pytest.mark.parametrize("epi", [0, 1, 2, 3, 4])
+def test_gemm_stream_k_tail(G, M, N, K, epi):
+    import torch
+
+    if M * K > 1e8 and epi not in (0, 4):
+        pytest.skip("largest shape checked with the bf16 and gated epilogues")
+    G.note(f"gemm_ws M={M} N={N} K={K} epi={epi}")
+    ws = torch.empty(G.B.gemm_workspace_bytes() // 4, dtype=torch.float32, device="cuda")
+    x, xh = G.bf16_dev((M, K), f"gx{M}{K}")
+    w, wh = G.bf16_dev((N, K), f"gw{N}{K}", 0.02)
+    bt = G.draw_normal(0, f"gb{N}", (N,), "f32", 0.02)
+    bias, bh = G.to_device(bt), bt.f64()
+    # every row of the last tile row (the tail tiles lie there) plus a sample of the rest
+    tail_rows = np.arange((M - 1) // 256 * 256, M)
+    rows = np.unique(np.concatenate([np.arange(64), tail_rows, np.random.default_rng(0).integers(0, M, 300)]))
+    lin = xh[rows] @ wh.T + bh                     # oracle: nn.Linear in float64
+    if epi in (0, 1):
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        G.B.op_gemm(x, w, bias, epi, out, workspace=ws)
+        G.sync()
+        got = G.to_f64(out)[rows]
+        ref = O.gelu_tanh(lin) if epi == 1 else lin
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+        assert G.rel_l2(got, ref) < 3e-3
+        # the workspace path differs from the plain one by fp32 summation order only
+        plain = torch.empty_like(out)
+        G.B.op_gemm(x, w, bias, epi, plain)
+        G.sync()
+        assert G.rel_l2(G.to_f64(out), G.to_f64(plain)) < 2e-3
+        return
+    x0t = G.draw_normal(0, f"gx0{M}{N}", (M, N), "f32")
+    out = G.to_device(x0t).clone()
+    x0 = x0t.f64()[rows]
+    if epi == 2:
+        G.B.op_gemm(x, w, bias, epi, out, workspace=ws)
+        ref = lin
+    elif epi == 3:
+        G.B.op_gemm(x, w, bias, epi, out, workspace=ws)
+        ref = x0 + lin
+    else:
+        L = 100
+        nsrc = (M + L - 1) // L
+        tab_t = G.draw_normal(0, "gtab", (N,), "f32", 0.5)
+        src_t = G.draw_normal(0, f"gsrc{nsrc}", (nsrc, 6 * N), "f32", 0.5)
+        src = G.to_device(src_t)
+        G.B.op_gemm(x, w, bias, epi, out, gate_tab=G.to_device(tab_t), gate_src=src[:, 2 * N:], gate_ld=6 * N,
+                    rows_per_gate=L, workspace=ws)
+        gate = tab_t.f64()[None, :] + src_t.f64()[rows // L, 2 * N:3 * N]
+        ref = x0 + lin * gate
+    G.sync()
+    got = G.to_f64(out)[rows]
+    assert G.rel_l2(got - x0 if epi != 2 else got, ref - x0 if epi != 2 else ref) < 1e-5
+    assert G.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max())
+
+
+def test_gemm_ws_rejects_bad_workspace(G):
+    import torch
+
+    x = torch.zeros((1024, 256), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((1024, 256), dtype=torch.bfloat16, device="cuda")
+    bias = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    out = torch.zeros((1024, 1024), dtype=torch.bfloat16, device="cuda")
+    short = torch.empty(16, dtype=torch.float32, device="cuda")
+    with pytest.raises(RuntimeError, match="workspace"):
+        G.B.op_gemm(x, w, bias, 0, out, workspace=short)
+
+
 # ------------------------------------------------------------------------------------------------
 # LayerNorm + modulation
 # ------------------------------------------------------------------------------------------------

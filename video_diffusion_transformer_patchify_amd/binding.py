@@ -74,6 +74,9 @@ _op_patchify = _sig("wan_op_patchify", [_vp, _i32, _i64, _i64, _i64, _i64, _i64,
 _op_unpatchify = _sig("wan_op_unpatchify", [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _i32, _vp])
 _op_gemm = _sig("wan_op_gemm", [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
                                 _vp])
+_op_gemm_ws = _sig("wan_op_gemm_ws", [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
+                                      _vp, _i64, _vp])
+_op_gemm_ws_bytes = _sig("wan_op_gemm_workspace_bytes", [], C.c_int64)
 _op_layernorm = _sig("wan_op_layernorm", [_vp, _i64, _i64, _f32, _i32, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp,
                                           _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp])
 _op_rope_table_floats = _sig("wan_op_rope_table_floats", [_i32] * 6, _i64)
@@ -112,7 +115,8 @@ _vae_op_rms_silu = _sig("wan_vae_op_rms_silu", [C.POINTER(_vp), C.POINTER(_vp), 
 
 EXPORTED = ["wan_dit_create", "wan_dit_forward", "wan_dit_forward_image", "wan_dit_denoise_step", "wan_dit_destroy", "wan_dit_last_error", "wan_dit_device_bytes",
             "wan_dit_time_attention", "wan_dit_attention_time",
-            "wan_op_patchify", "wan_op_unpatchify", "wan_op_cfg_euler", "wan_op_gemm", "wan_op_layernorm", "wan_op_rope_table_floats",
+            "wan_op_patchify", "wan_op_unpatchify", "wan_op_cfg_euler", "wan_op_gemm", "wan_op_gemm_ws",
+            "wan_op_gemm_workspace_bytes", "wan_op_layernorm", "wan_op_rope_table_floats",
             "wan_op_rope_table", "wan_op_qk_norm_rope", "wan_op_transpose_v", "wan_op_attention",
             "wan_op_attention_ws", "wan_op_attention_workspace_bytes", "wan_op_attention_noalloc",
             "wan_op_time_embed", "wan_probe_mfma",
@@ -293,13 +297,21 @@ def op_unpatchify(z: torch.Tensor, b: int, c: int, f: int, hz: int, wz: int, dty
 
 def op_gemm(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor, epilogue: int, out: torch.Tensor,
             gate_tab: torch.Tensor = None, gate_src: torch.Tensor = None, gate_ld: int = 0, rows_per_gate: int = 1,
-            stream=None):
+            stream=None, workspace: torch.Tensor = None):
+    """wan_op_gemm, or wan_op_gemm_ws with `workspace` (a device tensor of gemm_workspace_bytes() bytes)."""
     m, k = x.shape
     n = w.shape[0]
-    _check(_op_gemm(x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), bias.data_ptr(), m, n, k, epilogue,
-                    out.data_ptr(), out.stride(0), _ptr(gate_tab), _ptr(gate_src), gate_ld, rows_per_gate,
-                    _stream(stream)))
+    args = (x.data_ptr(), x.stride(0), w.data_ptr(), w.stride(0), bias.data_ptr(), m, n, k, epilogue, out.data_ptr(),
+            out.stride(0), _ptr(gate_tab), _ptr(gate_src), gate_ld, rows_per_gate)
+    if workspace is None:
+        _check(_op_gemm(*args, _stream(stream)))
+    else:
+        _check(_op_gemm_ws(*args, workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def gemm_workspace_bytes() -> int:
+    return int(_op_gemm_ws_bytes())
 
 
 def op_layernorm(x: torch.Tensor, eps: float, mode: int, out: torch.Tensor, tab_shift=None, tab_scale=None, src=None,

@@ -36,6 +36,12 @@ struct GemmArgs {
   int64_t gate_ld;
   int64_t rows_per_gate;   // tokens sharing one gate row (L for a per-sample timestep, 1 per-token)
   int tiles_m, tiles_n;
+  // persistent kernel: tiles [0, dp_tiles) of the grouped order run whole, in full rounds.  The rest
+  // (the stream-K tail: sk_tiles < one round) run as sk_split K chunks each, workgroup w < sk_tiles *
+  // sk_split taking chunk w % sk_split of tail tile w / sk_split; each chunk writes its unbiased fp32
+  // partial tile [256][256] to sk_part + 65536 w, and k_gemm_sk_fix sums them and applies the epilogue.
+  int dp_tiles, sk_tiles, sk_split;
+  float* sk_part;
 };
 
 // Dispatch order places consecutive workgroups on different XCDs (round robin over 8).  Renumber so
@@ -220,6 +226,28 @@ constexpr int SLOTS_PER_XCD = 32;                // CUs per XCD: one persistent 
 
 __device__ __forceinline__ int row_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
+// Tile tt of the grouped order: GROUP_M tile rows at a time, column by column within a group.
+__device__ __forceinline__ void tile_coords(const GemmArgs& a, int tt, int& tm, int& tn) {
+  const int width = GROUP_M * a.tiles_n;
+  const int first_m = (tt / width) * GROUP_M;
+  const int gsz = min(a.tiles_m - first_m, GROUP_M);
+  tm = first_m + (tt % width) % gsz;
+  tn = (tt % width) / gsz;
+}
+
+// Stream-K chunk of a wave's 128 x 128 block: the raw fp32 sums into the partial tile [256][256]
+// (element (m, n) of the tile at m * 256 + n).
+__device__ __forceinline__ void store_partial(float* part, const f32x16 (&acc)[4][4], int wm0, int wn0, int l32, int g) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        *(f32x4*)(part + (wm0 + 32 * j + l32) * BIG + wn0 + 32 * i + 8 * rg + 4 * g) =
+            (f32x4){acc[i][j][4 * rg], acc[i][j][4 * rg + 1], acc[i][j][4 * rg + 2], acc[i][j][4 * rg + 3]};
+}
+
 // bf16 epilogue of one wave's 128 x 128 block (bias already in the accumulators) through its LDS slice,
 // 32 rows at a time.  Writes: lane (l32, g) puts its 4 values of chunk c (= 8 output columns) of row l32
 // into 16-byte position c ^ (l32 & 15), 8-byte half g ^ (l32 >> 4) (conflict-free); reads: 16 lanes per
@@ -269,7 +297,9 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& a, const f32x16 (
   }
 }
 
-template <int EPI>
+// SK: the stream-K launch.  Workgroup w takes K stages [kb, kb + nk) of chunk w % sk_split of tail tile
+// dp_tiles + w / sk_split and writes the raw sums (no bias) to its partial tile.
+template <int EPI, bool SK>
 __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[NSTAGE * STAGE_BYTES + 4 * EPI_SLICE];
   // the wave index is uniform: read it into a scalar register so every LDS address of the direct
@@ -278,14 +308,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
 
-  // ---- this workgroup's tiles: XCD blockIdx % 8 owns tiles [lo, hi) of the grouped order; its
-  //      SLOTS_PER_XCD workgroups take every SLOTS_PER_XCD-th one
-  const int ntiles = a.tiles_m * a.tiles_n;
-  const int per = (ntiles + 7) / 8;
+  // ---- this workgroup's tiles: XCD blockIdx % 8 owns tiles [lo, hi) of the first dp_tiles of the
+  //      grouped order; its SLOTS_PER_XCD workgroups take every SLOTS_PER_XCD-th one
+  const int per = (a.dp_tiles + 7) / 8;
   const int lo = (blockIdx.x % 8) * per;
-  const int hi = min(ntiles, lo + per);
+  const int hi = min(a.dp_tiles, lo + per);
   int t = lo + (int)(blockIdx.x / 8);
-  if (t >= hi) return;
+  int kb = 0, nk = (int)(a.K / BK4);   // >= 4 (checked by the launcher)
+  if constexpr (SK) {
+    const int c = (int)blockIdx.x % a.sk_split;
+    t = a.dp_tiles + (int)blockIdx.x / a.sk_split;
+    kb = (int)((int64_t)c * nk / a.sk_split);
+    nk = (int)((int64_t)(c + 1) * nk / a.sk_split) - kb;   // >= 4 (the launcher's split)
+  } else {
+    if (t >= hi) return;
+  }
 
   int64_t m0, n0;
   uint32_t xo[4], wo[4];
@@ -294,12 +331,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   // tile t: origin, and per-lane direct-load offsets.  Instruction I = 4 wave + i covers tile rows
   // 16 I .. 16 I + 15: lane -> row 16 I + lane / 4, LDS chunk lane % 4, global chunk (lane % 4) ^ swz(row).
   // Rows past M or N repeat the last row (their results are never stored).
-  auto setup = [&](int tt) {
-    const int width = GROUP_M * a.tiles_n;
-    const int first_m = (tt / width) * GROUP_M;
-    const int gsz = min(a.tiles_m - first_m, GROUP_M);
-    const int tm = first_m + (tt % width) % gsz;
-    const int tn = (tt % width) / gsz;
+  // kb: first K stage (stream-K chunks)
+  auto setup = [&](int tt, int kb) {
+    int tm, tn;
+    tile_coords(a, tt, tm, tn);
     m0 = (int64_t)tm * BIG;
     n0 = (int64_t)tn * BIG;
 #pragma unroll
@@ -312,8 +347,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
       xo[i] = (uint32_t)(((rx - m0) * a.ldx + cchunk * 8) * 2);
       wo[i] = (uint32_t)(((rw - n0) * a.ldw + cchunk * 8) * 2);
     }
-    xt = (const char*)(a.x + m0 * a.ldx);
-    wt = (const char*)(a.w + n0 * a.ldw);
+    xt = (const char*)(a.x + m0 * a.ldx + (int64_t)kb * BK4);
+    wt = (const char*)(a.w + n0 * a.ldw + (int64_t)kb * BK4);
   };
   // instruction i of half h of stage kt: h = 0 the X tile, h = 1 the W tile
   auto dma = [&](int kt, int h, int i) {
@@ -343,7 +378,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   // bf16 epilogues: the accumulators start from the bias, written by one MFMA each at tile start:
   // A holds column n's bias split into bf16 hi + lo at k = 0, 1 (lane l32 of block i is column
   // wn0 + 32 i + l32), B holds 1 at k = 0, 1, so D[n][m] = hi + lo = bias[n] to ~2^-18 relative.
-  constexpr bool FOLD = EPI == EPI_BF16 || EPI == EPI_GELU_BF16;
+  // (stream-K chunks start from zero: k_gemm_sk_fix adds the bias once)
+  constexpr bool FOLD = !SK && (EPI == EPI_BF16 || EPI == EPI_GELU_BF16);
   float bcol[4];
   auto bias_cols = [&](int64_t nb, int i) {   // bias of column nb + 32 i + l32 (clamped past N)
     const int64_t n = nb + 32 * i + l32;
@@ -405,10 +441,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
   using W2 = std::integral_constant<int, 2>;
   using W1 = std::integral_constant<int, 1>;
   using W0 = std::integral_constant<int, 0>;
-  const int nk = (int)(a.K / BK4);       // >= 4 (checked by the launcher)
   char* slice = lds + NSTAGE * STAGE_BYTES + wave * EPI_SLICE;
 
-  setup(t);
+  setup(t, kb);
   if constexpr (FOLD) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) bcol[i] = bias_cols(n0 + wn0, i);
@@ -440,14 +475,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) frag(0, 0, q);
     const int tnext = t + SLOTS_PER_XCD;
-    const bool more = tnext < hi;
+    const bool more = !SK && tnext < hi;
     if constexpr (FOLD) {
       // the next tile's columns (after the last tile: this tile's again, loaded and never used)
-      const int tt = more ? tnext : t;
-      const int width = GROUP_M * a.tiles_n;
-      const int first_m = (tt / width) * GROUP_M;
-      const int gsz = min(a.tiles_m - first_m, GROUP_M);
-      bias_nb = (int64_t)((tt % width) / gsz) * BIG + wn0;
+      int tm, tn;
+      tile_coords(a, more ? tnext : t, tm, tn);
+      bias_nb = (int64_t)tn * BIG + wn0;
     }
     int kt = 0;
     for (; kt + 4 < nk; ++kt) step(kt, T{}, T{}, W2{}, T{}, F{});
@@ -460,15 +493,48 @@ __global__ __launch_bounds__(256, 1) void k_gemm_big(GemmArgs a) {
     // every wave has read its last fragments before any wave refills the stages
     block_sync();
     if (more) {
-      setup(tnext);
+      setup(tnext, 0);
       prologue();
     }
-    if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16)
+    if constexpr (SK)
+      store_partial(a.sk_part + (int64_t)blockIdx.x * BIG * BIG, acc, wm0, wn0, l32, g);
+    else if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16)
       store_tile_lds<EPI>(a, acc, tm0 + wm0, tn0 + wn0, slice, lane, l32, g);
     else
       store_tile<EPI, 4, 4>(a, acc, tm0 + wm0, tn0 + wn0, l32, g);
     if (!more) break;
     t = tnext;
+  }
+}
+
+// Stream-K fix-up: per tail tile, the sum of its sk_split fp32 partial tiles (in chunk order), plus the
+// bias, through the epilogue.  64 workgroups per tile, each 4 rows x 256 columns, 4 columns per thread.
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_sk_fix(GemmArgs a) {
+  const int tl = (int)blockIdx.x / 64;
+  int tm, tn;
+  tile_coords(a, a.dp_tiles + tl, tm, tn);
+  const int r = 4 * ((int)blockIdx.x % 64) + (int)(threadIdx.x >> 6), c = 4 * (int)(threadIdx.x & 63);
+  const int64_t m = (int64_t)tm * BIG + r, n = (int64_t)tn * BIG + c;
+  if (m >= a.M || n >= a.N) return;   // N is a multiple of 8: a thread's 4 columns are all in or all out
+  const float* p = a.sk_part + (int64_t)tl * a.sk_split * BIG * BIG + r * BIG + c;
+  f32x4 v = *(const f32x4*)(a.bias + n);
+  for (int k = 0; k < a.sk_split; ++k) v += *(const f32x4*)(p + (int64_t)k * BIG * BIG);
+  if constexpr (EPI == EPI_BF16 || EPI == EPI_GELU_BF16) {
+    if constexpr (EPI == EPI_GELU_BF16) {
+      v.x = gelu_tanh_f(v.x); v.y = gelu_tanh_f(v.y); v.z = gelu_tanh_f(v.z); v.w = gelu_tanh_f(v.w);
+    }
+    *(u32x2*)((bf16_t*)a.out + m * a.ldo + n) = (u32x2){pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+  } else {
+    float* o = (float*)a.out + m * a.ldo + n;
+    if constexpr (EPI == EPI_F32) {
+      *(f32x4*)o = v;
+    } else if constexpr (EPI == EPI_RES_F32) {
+      *(f32x4*)o = *(const f32x4*)o + v;
+    } else {
+      const f32x4 gate = *(const f32x4*)(a.gate_tab + n) + *(const f32x4*)(a.gate_src + (m / a.rows_per_gate) * a.gate_ld + n);
+      *(f32x4*)o = *(const f32x4*)o + v * gate;
+    }
   }
 }
 
@@ -488,16 +554,41 @@ hipError_t launch_tile(int epi, GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_big(int epi, GemmArgs& a, hipStream_t s) {
+// The persistent kernel runs one workgroup per CU slot (8 XCDs x 32), so a launch takes
+// ceil(tiles / 256) rounds of whole tiles.  With a workspace and a last round at most half full, the
+// tiles of that round are split along K instead (as many chunks as fill the slots, at least 4 stages
+// each) and a fix-up pass sums them: the launch then costs its full rounds plus a fraction of one.
+hipError_t launch_big(int epi, GemmArgs& a, float* ws, int64_t ws_bytes, hipStream_t s) {
   a.tiles_m = (int)ceil_div(a.M, BIG);
   a.tiles_n = (int)ceil_div(a.N, BIG);
-  dim3 grid(8 * SLOTS_PER_XCD), block(256);
+  const int slots = 8 * SLOTS_PER_XCD;
+  const int ntiles = a.tiles_m * a.tiles_n;
+  const int tail = ntiles % slots;
+  const int nk = (int)(a.K / BK4);
+  int split = 0;
+  if (ws != nullptr && tail > 0 && 2 * tail <= slots) {
+    split = min(slots / tail, nk / 4);
+    if (split < 2 || (int64_t)tail * split * BIG * BIG * 4 > ws_bytes) split = 0;
+  }
+  a.dp_tiles = split ? ntiles - tail : ntiles;
+  a.sk_tiles = split ? tail : 0;
+  a.sk_split = split ? split : 1;
+  a.sk_part = split ? ws : nullptr;
+  dim3 grid(slots), block(256);
+  auto run = [&](auto epi_tag) {
+    constexpr int E = decltype(epi_tag)::value;
+    hipLaunchKernelGGL((k_gemm_big<E, false>), grid, block, 0, s, a);
+    if (split) {
+      hipLaunchKernelGGL((k_gemm_big<E, true>), dim3((unsigned)(tail * split)), block, 0, s, a);
+      hipLaunchKernelGGL(k_gemm_sk_fix<E>, dim3((unsigned)(tail * 64)), block, 0, s, a);
+    }
+  };
   switch (epi) {
-    case EPI_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_BF16>, grid, block, 0, s, a); break;
-    case EPI_GELU_BF16: hipLaunchKernelGGL(k_gemm_big<EPI_GELU_BF16>, grid, block, 0, s, a); break;
-    case EPI_F32: hipLaunchKernelGGL(k_gemm_big<EPI_F32>, grid, block, 0, s, a); break;
-    case EPI_RES_F32: hipLaunchKernelGGL(k_gemm_big<EPI_RES_F32>, grid, block, 0, s, a); break;
-    case EPI_GATE_F32: hipLaunchKernelGGL(k_gemm_big<EPI_GATE_F32>, grid, block, 0, s, a); break;
+    case EPI_BF16: run(std::integral_constant<int, EPI_BF16>{}); break;
+    case EPI_GELU_BF16: run(std::integral_constant<int, EPI_GELU_BF16>{}); break;
+    case EPI_F32: run(std::integral_constant<int, EPI_F32>{}); break;
+    case EPI_RES_F32: run(std::integral_constant<int, EPI_RES_F32>{}); break;
+    case EPI_GATE_F32: run(std::integral_constant<int, EPI_GATE_F32>{}); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -647,7 +738,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_f32m(const float* __restrict__ 
 
 hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64_t ldw, const float* bias, int64_t M,
                             int64_t N, int64_t K, int epi, void* out, int64_t ldo, const float* gate_tab,
-                            const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, hipStream_t s) {
+                            const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, hipStream_t s, float* ws,
+                            int64_t ws_bytes) {
   if (M <= 0 || N <= 0) return hipSuccess;
   GemmArgs a;
   a.x = x; a.ldx = ldx; a.w = w; a.ldw = ldw; a.bias = bias;
@@ -661,9 +753,11 @@ hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64
   const int64_t big_tiles = ceil_div(M, 256) * ceil_div(N, 256);
   const bool offsets_fit = 256 * (ldx > ldw ? ldx : ldw) * 2 < (1LL << 31);
   const bool aligned = N % 8 == 0 && ldo % 8 == 0 && ((uintptr_t)out & 15) == 0;
-  if (big_tiles >= 512 && offsets_fit && K % 32 == 0 && K >= 128 && aligned) return launch_big(epi, a, s);
+  if (big_tiles >= 512 && offsets_fit && K % 32 == 0 && K >= 128 && aligned) return launch_big(epi, a, ws, ws_bytes, s);
   return launch_tile<128, 128, 64, 64>(epi, a, s);
 }
+
+int64_t gemm_workspace_bytes() { return (int64_t)8 * SLOTS_PER_XCD * BIG * BIG * 4; }
 
 hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, int64_t M,
                            int64_t N, int64_t K, float* C, int64_t ldc, int silu_in, int silu_out, hipStream_t s) {

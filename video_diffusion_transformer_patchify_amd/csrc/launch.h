@@ -21,7 +21,10 @@ hipError_t launch_pack_f32(const void* src, int dtype, int64_t n, float* dst, hi
 
 hipError_t launch_gemm_bf16(const bf16_t* x, int64_t ldx, const bf16_t* w, int64_t ldw, const float* bias, int64_t M,
                             int64_t N, int64_t K, int epi, void* out, int64_t ldo, const float* gate_tab,
-                            const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, hipStream_t s);
+                            const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, hipStream_t s,
+                            float* ws = nullptr, int64_t ws_bytes = 0);
+// workspace of launch_gemm_bf16's stream-K tail: fp32 partial tiles of at most one round
+int64_t gemm_workspace_bytes();
 hipError_t launch_gemm_f32(const float* A, int64_t lda, const float* W, int64_t ldw, const float* bias, int64_t M,
                            int64_t N, int64_t K, float* C, int64_t ldc, int silu_in, int silu_out, hipStream_t s);
 

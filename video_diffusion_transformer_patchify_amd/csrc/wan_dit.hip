@@ -91,6 +91,8 @@ struct wan_dit {
   float *x, *z, *t_s, *t_h, *temb, *tproj, *rope, *t_dup;
   float* attn_ws;   // key-split partials of the attention's last round and its redo flags
   int64_t attn_ws_bytes = 0;
+  float* gemm_ws;   // stream-K partial tiles of the GEMMs' last round
+  int64_t gemm_ws_bytes = 0;
   int64_t ldv_max, ldv2_max, ldvi_max, rows_max, trows_max;
   // opt-in timing of the self-attention launches (wan_dit_time_attention): event pairs, start then end
   std::vector<hipEvent_t> att_ev;
@@ -262,6 +264,8 @@ void plan_workspace(wan_dit* h, Arena& ar) {
   h->t_dup = ar.take<float>(c.max_batch * (c.per_token_timestep ? c.max_tokens : 1));
   h->attn_ws_bytes = attention_workspace_bytes(c.max_batch, c.max_tokens, c.num_heads);
   h->attn_ws = ar.take<float>(h->attn_ws_bytes / 4);
+  h->gemm_ws_bytes = gemm_workspace_bytes();
+  h->gemm_ws = ar.take<float>(h->gemm_ws_bytes / 4);
 }
 
 void release_events(wan_dit* h) {
@@ -635,8 +639,8 @@ wan_status enqueue_forward(wan_dit* h, const FwdIn& in, const FwdOut& fo, hipStr
     // self-attention
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 0 * D, b.table + 1 * D, h->tproj, 6 * D, 0 * D, 1 * D,
                              rows_per_mod, nullptr, nullptr, res_mode, h->br, res_tab, res_src, 6 * D, h->y, s), "norm1");
-    HIP_TRY(launch_gemm_bf16(h->y, D, b.wqkv, D, b.bqkv, M, 3 * D, D, EPI_BF16, h->qkv, 3 * D, nullptr, nullptr, 0, 1, s),
-            "qkv");
+    HIP_TRY(launch_gemm_bf16(h->y, D, b.wqkv, D, b.bqkv, M, 3 * D, D, EPI_BF16, h->qkv, 3 * D, nullptr, nullptr, 0, 1, s,
+                             h->gemm_ws, h->gemm_ws_bytes), "qkv");
     HIP_TRY(launch_rms_rope(h->qkv, 3 * D, M, D, eps, 0, b.gq, D, b.gk, h->rope, L, (int)in.Fp, (int)in.Hp, (int)in.Wp, dt, dh,
                             dw, s, qs), "qk norm rope");
     HIP_TRY(launch_transpose_v(h->qkv, 3 * D, 2 * D, B, L, (int)nh, h->vt, ldv, s), "v transpose");
@@ -645,12 +649,14 @@ wan_status enqueue_forward(wan_dit* h, const FwdIn& in, const FwdOut& fo, hipStr
     HIP_TRY(launch_attention(h->qkv, 3 * D, h->qkv + D, 3 * D, h->vt, ldv, h->attn, D, B, L, L, (int)nh, true, s,
                              h->attn_ws, h->attn_ws_bytes, true), "self attention");
     if (timed) HIP_TRY(hipEventRecord(h->att_ev[2 * h->att_used++ + 1], s), "self attention timing");
-    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn1 out");
+    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo, D, b.bo, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s,
+                             h->gemm_ws, h->gemm_ws_bytes), "attn1 out");
     // cross-attention: x += gate1 * attn, then norm2 (affine)
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 1, nullptr, nullptr, nullptr, 0, 0, 0, rows_per_mod, b.n2w, b.n2b, 2, h->br,
                              b.table + 2 * D, h->tproj + 2 * D, 6 * D, h->y, s), "norm2");
     bf16_t* q2 = h->qkv;
-    HIP_TRY(launch_gemm_bf16(h->y, D, b.wq2, D, b.bq2, M, D, D, EPI_BF16, q2, D, nullptr, nullptr, 0, 1, s), "q2");
+    HIP_TRY(launch_gemm_bf16(h->y, D, b.wq2, D, b.bq2, M, D, D, EPI_BF16, q2, D, nullptr, nullptr, 0, 1, s,
+                             h->gemm_ws, h->gemm_ws_bytes), "q2");
     HIP_TRY(launch_rms_rope(q2, D, M, D, eps, 0, b.gq2, 0, nullptr, nullptr, L, 1, 1, 1, dt, dh, dw, s, qs), "q2 norm");
     HIP_TRY(launch_gemm_bf16(h->ctx, D, b.wkv2, D, b.bkv2, B * Lt, 2 * D, D, EPI_BF16, h->kv2, 2 * D, nullptr, nullptr, 0, 1, s),
             "kv2");
@@ -668,12 +674,15 @@ wan_status enqueue_forward(wan_dit* h, const FwdIn& in, const FwdOut& fo, hipStr
       HIP_TRY(launch_attention(q2, D, h->kvi, 2 * D, h->vti, ldvi, h->attn, D, B, L, Li, (int)nh, false, s, h->attn_ws,
                                h->attn_ws_bytes, true, true), "image cross attention");
     }
-    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "attn2 out");
+    HIP_TRY(launch_gemm_bf16(h->attn, D, b.wo2, D, b.bo2, M, D, D, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s,
+                             h->gemm_ws, h->gemm_ws_bytes), "attn2 out");
     // feed-forward: x += cross-attn (ungated), then norm3 + modulation
     HIP_TRY(launch_layernorm(h->x, M, D, eps, 0, b.table + 3 * D, b.table + 4 * D, h->tproj, 6 * D, 3 * D, 4 * D,
                              rows_per_mod, nullptr, nullptr, 1, h->br, nullptr, nullptr, 0, h->y, s), "norm3");
-    HIP_TRY(launch_gemm_bf16(h->y, D, b.w1, D, b.b1, M, Fd, D, EPI_GELU_BF16, h->hbuf, Fd, nullptr, nullptr, 0, 1, s), "ffn1");
-    HIP_TRY(launch_gemm_bf16(h->hbuf, Fd, b.w2, Fd, b.b2, M, D, Fd, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s), "ffn2");
+    HIP_TRY(launch_gemm_bf16(h->y, D, b.w1, D, b.b1, M, Fd, D, EPI_GELU_BF16, h->hbuf, Fd, nullptr, nullptr, 0, 1, s,
+                             h->gemm_ws, h->gemm_ws_bytes), "ffn1");
+    HIP_TRY(launch_gemm_bf16(h->hbuf, Fd, b.w2, Fd, b.b2, M, D, Fd, EPI_BF16, h->br, D, nullptr, nullptr, 0, 1, s,
+                             h->gemm_ws, h->gemm_ws_bytes), "ffn2");
     res_mode = 2;
     res_tab = b.table + 5 * D;
     res_src = h->tproj + 5 * D;
@@ -803,10 +812,10 @@ extern "C" wan_status wan_op_cfg_euler(const float* z, int64_t ldz, int64_t C, i
   return WAN_OK;
 }
 
-extern "C" wan_status wan_op_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int64_t M,
-                                  int64_t N, int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
-                                  const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, void* stream) {
-  g_err.clear();
+// Argument checks shared by wan_op_gemm and wan_op_gemm_ws.
+static wan_status check_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int64_t M,
+                             int64_t N, int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
+                             const float* gate_src, int64_t gate_ld, int64_t rows_per_gate) {
   REQUIRE(epilogue >= 0 && epilogue <= 4, WAN_ERR_INVALID_ARG, "gemm: bad epilogue %d", epilogue);
   REQUIRE(M >= 0 && N > 0 && K > 0, WAN_ERR_SHAPE, "gemm: bad sizes");
   REQUIRE(K % 64 == 0, WAN_ERR_SHAPE, "gemm: K must be a multiple of 64");
@@ -816,8 +825,36 @@ extern "C" wan_status wan_op_gemm(const void* x, int64_t ldx, const void* w, int
   REQUIRE(x && w && bias && out, WAN_ERR_INVALID_ARG, "gemm: NULL pointer");
   REQUIRE(epilogue != EPI_GATE_F32 || (gate_tab && gate_src && rows_per_gate > 0 && gate_ld >= N), WAN_ERR_INVALID_ARG,
           "gemm: gate epilogue needs gate_tab, gate_src, gate_ld >= N and rows_per_gate > 0");
+  return WAN_OK;
+}
+
+extern "C" wan_status wan_op_gemm(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int64_t M,
+                                  int64_t N, int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
+                                  const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, void* stream) {
+  g_err.clear();
+  const wan_status st = check_gemm(x, ldx, w, ldw, bias, M, N, K, epilogue, out, ldo, gate_tab, gate_src, gate_ld,
+                                   rows_per_gate);
+  if (st != WAN_OK) return st;
   HIP_TRY(launch_gemm_bf16((const bf16_t*)x, ldx, (const bf16_t*)w, ldw, bias, M, N, K, epilogue, out, ldo, gate_tab, gate_src,
                            gate_ld, rows_per_gate, (hipStream_t)stream), "gemm");
+  return WAN_OK;
+}
+
+extern "C" int64_t wan_op_gemm_workspace_bytes(void) { return gemm_workspace_bytes(); }
+
+extern "C" wan_status wan_op_gemm_ws(const void* x, int64_t ldx, const void* w, int64_t ldw, const float* bias, int64_t M,
+                                     int64_t N, int64_t K, int32_t epilogue, void* out, int64_t ldo, const float* gate_tab,
+                                     const float* gate_src, int64_t gate_ld, int64_t rows_per_gate, void* workspace,
+                                     int64_t workspace_bytes, void* stream) {
+  g_err.clear();
+  const wan_status st = check_gemm(x, ldx, w, ldw, bias, M, N, K, epilogue, out, ldo, gate_tab, gate_src, gate_ld,
+                                   rows_per_gate);
+  if (st != WAN_OK) return st;
+  REQUIRE(workspace != nullptr && ((uintptr_t)workspace & 15) == 0 && workspace_bytes >= gemm_workspace_bytes(),
+          WAN_ERR_INVALID_ARG, "gemm_ws: workspace must be 16-byte aligned and >= %lld bytes",
+          (long long)gemm_workspace_bytes());
+  HIP_TRY(launch_gemm_bf16((const bf16_t*)x, ldx, (const bf16_t*)w, ldw, bias, M, N, K, epilogue, out, ldo, gate_tab, gate_src,
+                           gate_ld, rows_per_gate, (hipStream_t)stream, (float*)workspace, workspace_bytes), "gemm_ws");
   return WAN_OK;
 }
 
