@@ -201,6 +201,59 @@ __global__ __launch_bounds__(256, 1) void k_vae_conv(const VaeConvArgs a) {
         else ((float*)a.video)[idx] = v;
       }
     }
+  } else if (a.nout[j] != nullptr) {
+    // one channel tile holds every channel of the lane's pixel: 16 per fragment in this lane, the other
+    // 16 in lane l32 + 32 (1 - kh).  The norm is taken over the bf16-rounded outputs, as a separate
+    // norm pass reading them back would take it.
+    const int64_t wp = a.W + 2;
+    const int64_t plane_out = (int64_t)(a.H + 2) * wp * 16;
+    const bf16_t* rp = a.res[j];
+    bf16_t* op = a.out[j];
+    bf16_t* np = a.nout[j];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int y = y0 + 4 * wave + r;
+      const bool ok = y < a.H && x < a.W;
+      const int64_t pix = ((int64_t)(min(y, a.H - 1) + 1) * wp + (min(x, a.W - 1) + 1)) * 16;
+      u32x2 o[NCF][4];
+      float ss = 0.0f;
+#pragma unroll
+      for (int f = 0; f < NCF; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int co = f * 32 + 8 * q + 4 * kh;
+          const int64_t off = (int64_t)(co >> 4) * plane_out + pix + (co & 15);
+          float v0 = acc[f][r][4 * q], v1 = acc[f][r][4 * q + 1], v2 = acc[f][r][4 * q + 2], v3 = acc[f][r][4 * q + 3];
+          if (rp) {
+            const u32x2 rv = *(const u32x2*)(rp + off);
+            v0 += lo_bf16(rv.x); v1 += hi_bf16(rv.x); v2 += lo_bf16(rv.y); v3 += hi_bf16(rv.y);
+          }
+          o[f][q].x = pack_bf16x2(v0, v1);
+          o[f][q].y = pack_bf16x2(v2, v3);
+          const float u0 = lo_bf16(o[f][q].x), u1 = hi_bf16(o[f][q].x), u2 = lo_bf16(o[f][q].y), u3 = hi_bf16(o[f][q].y);
+          ss = fmaf(u0, u0, ss);
+          ss = fmaf(u1, u1, ss);
+          ss = fmaf(u2, u2, ss);
+          ss = fmaf(u3, u3, ss);
+        }
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);   // both halves, in the same order in both lanes
+      const float rstd = 1.0f / sqrtf(fmaf(ss, 1.0f / (float)(32 * NCF), a.neps));
+      if (!ok) continue;
+#pragma unroll
+      for (int f = 0; f < NCF; ++f)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int co = f * 32 + 8 * q + 4 * kh;
+          const int64_t off = (int64_t)(co >> 4) * plane_out + pix + (co & 15);
+          if (!a.nonly) *(u32x2*)(op + off) = o[f][q];
+          const f32x4 g = *(const f32x4*)(a.ngamma + co);
+          u32x2 w;
+          w.x = pack_bf16x2(silu_f(lo_bf16(o[f][q].x) * rstd * g.x), silu_f(hi_bf16(o[f][q].x) * rstd * g.y));
+          w.y = pack_bf16x2(silu_f(lo_bf16(o[f][q].y) * rstd * g.z), silu_f(hi_bf16(o[f][q].y) * rstd * g.w));
+          *(u32x2*)(np + off) = w;
+        }
+    }
   } else {
     const int64_t wp = a.W + 2;
     const int64_t plane_out = (int64_t)(a.H + 2) * wp * 16;

@@ -31,6 +31,12 @@ struct VaeConvArgs {
   int32_t tiles_x, tiles_y;
   int32_t video_T;                 // frames of the video output
   int32_t video_bf16;              // video dtype: 1 bf16, 0 fp32
+  // fused RMS norm + SiLU of the (bf16-rounded) output over its 32 * ncf channels, for a launch with one
+  // output-channel tile and no split: nout[j] = SiLU(ngamma * u / sqrt(mean(u^2) + neps)).  Null: none.
+  bf16_t* nout[VAE_MAXF];
+  const float* ngamma;             // [32 * ncf]
+  float neps;
+  int32_t nonly;                   // 1: only nout is written (out is not)
 };
 
 // kt: 1 or 3 time taps; ks: 1 or 3 (square) spatial taps; up: input is the half-size frame, read through

@@ -340,8 +340,29 @@ void norm_launch(Ctx& x, const bf16_t* const* in, bf16_t* const* out, int nf, in
   x.chk(launch_vae_rms_silu(in, out, nf, c, cpad(c) / 16, x.H[st], x.W[st], g, x.h->cfg.eps, x.s));
 }
 
+// A convolution whose one output-channel tile holds all of its channels (stage D: 96 channels in one
+// workgroup) applies the RMS norm + SiLU that follows it in its own epilogue.
+bool fusable(const ConvW& c) { return c.cout == 32 * c.ncf && c.ntiles() == 1; }
+
+void fuse_norm(const Ctx& x, VaeConvArgs& a, bf16_t* const* nout, int n, const float* g, bool only) {
+  for (int j = 0; j < n; ++j) a.nout[j] = nout[j];
+  a.ngamma = g;
+  a.neps = x.h->cfg.eps;
+  a.nonly = only ? 1 : 0;
+}
+
+// Slots of the current frames in ring q at stage st.
+void ring_slots(const Ctx& x, const Seq& q, int st, int n, bf16_t** dst) {
+  const int64_t fe = vae_frame_elems(q.c, x.H[st], x.W[st]);
+  for (int j = 0; j < n; ++j) dst[j] = q.slot(q.hist + j, fe);
+}
+
 // One residual block on n frames: in[j] -> out[j] (in == out unless the block has a shortcut).
-void res_block(Ctx& x, size_t i, bf16_t* const* in, bf16_t* const* out, bf16_t* hbuf, int n) {
+// in_normed: the producer of `in` already wrote norm1's output into this block's first ring.  next_g,
+// next_nout: the norm that follows the block (the next block's norm1 or the head's), applied in conv2's
+// epilogue where it can be; the return value says whether it was.
+bool res_block(Ctx& x, size_t i, bf16_t* const* in, bf16_t* const* out, bf16_t* hbuf, int n, bool in_normed = false,
+               const float* next_g = nullptr, bf16_t* const* next_nout = nullptr) {
   wan_vae* h = x.h;
   const ResW& r = h->res[i];
   Seq& q1 = h->n1[i];
@@ -358,12 +379,14 @@ void res_block(Ctx& x, size_t i, bf16_t* const* in, bf16_t* const* out, bf16_t* 
     p2[j] = q2.slot(q2.hist + j, fe2);
     ph[j] = hbuf + j * feh;
   }
-  norm_launch(x, in, p1, n, r.ci, st, r.g1);
+  if (!in_normed) norm_launch(x, in, p1, n, r.ci, st, r.g1);
   VaeConvArgs a1{};
   ring_inputs(x, q1, st, n, a1);
   for (int j = 0; j < n; ++j) a1.out[j] = ph[j];
+  const bool fuse1 = fusable(r.c1);
+  if (fuse1) fuse_norm(x, a1, p2, n, r.g2, true);   // conv1's output is only norm2's input
   conv_launch(x, r.c1, a1, st, n, 0, 1, false);
-  norm_launch(x, ph, p2, n, r.co, st, r.g2);
+  if (!fuse1) norm_launch(x, ph, p2, n, r.co, st, r.g2);
   if (r.has_sc) {
     VaeConvArgs as{};
     for (int j = 0; j < n; ++j) {
@@ -378,13 +401,18 @@ void res_block(Ctx& x, size_t i, bf16_t* const* in, bf16_t* const* out, bf16_t* 
     a2.out[j] = out[j];
     a2.res[j] = out[j];
   }
+  const bool fuse2 = next_nout != nullptr && fusable(r.c2);
+  if (fuse2) fuse_norm(x, a2, next_nout, n, next_g, false);
   conv_launch(x, r.c2, a2, st, n, 0, 1, false);
+  return fuse2;
 }
 
 // upsample3d / upsample2d of n input frames at stage st: time conv (not on the first chunk), then the
-// nearest x2 + 3x3 conv into dst frames at stage st + 1.
+// nearest x2 + 3x3 conv into dst frames at stage st + 1.  next_g, next_nout: the norm that follows,
+// applied in that conv's epilogue where it can be (*normed says whether it was).
 int upsample(Ctx& x, const UpW& u, Seq* ring, bf16_t* const* in, int n, int st, bool first, bf16_t* tbuf,
-             bf16_t* const* dst) {
+             bf16_t* const* dst, const float* next_g = nullptr, bf16_t* const* next_nout = nullptr,
+             bool* normed = nullptr) {
   const bf16_t* src[2 * VAE_MAXF];
   int m = n;
   if (u.time && !first) {
@@ -403,7 +431,10 @@ int upsample(Ctx& x, const UpW& u, Seq* ring, bf16_t* const* in, int n, int st, 
     ar.in[j][0] = src[j];
     ar.out[j] = dst[j];
   }
+  const bool fuse = next_nout != nullptr && fusable(u.rs);
+  if (fuse) fuse_norm(x, ar, next_nout, m, next_g, false);
   conv_launch(x, u.rs, ar, st + 1, m, 1, 1, false);
+  if (normed) *normed = fuse;
   return m;
 }
 
@@ -447,14 +478,21 @@ void decode_chunk(Ctx& x, const void* z, int zdt, int64_t F, int64_t f0, int n, 
   upsample(x, h->up[1], &h->xb, pb, nB, 1, first, h->tb, pc);
   for (; ri < 11; ++ri) res_block(x, ri, pc, pc, h->hc, nD);                 // up block 2
   for (int j = 0; j < nD; ++j) pd[j] = h->xd + j * x.fe(b, 3);
-  upsample(x, h->up[2], nullptr, pc, nD, 2, first, nullptr, pd);
-  for (; ri < 14; ++ri) res_block(x, ri, pd, pd, h->hd, nD);                 // up block 3
+  // stage D: each norm runs in the epilogue of the convolution before it (96 channels per workgroup)
+  bf16_t* pn[VAE_MAXF];
+  ring_slots(x, h->n1[ri], 3, nD, pn);
+  bool normed = false;
+  upsample(x, h->up[2], nullptr, pc, nD, 2, first, nullptr, pd, h->res[ri].g1, pn, &normed);
+  for (; ri < 14; ++ri) {                                                     // up block 3
+    const bool last = ri + 1 == 14;
+    ring_slots(x, last ? h->nout : h->n1[ri + 1], 3, nD, pn);
+    normed = res_block(x, ri, pd, pd, h->hd, nD, normed, last ? h->g_out : h->res[ri + 1].g1, pn);
+  }
   // head: RMS_norm + SiLU -> conv_out into the video frames t0 .. t0 + nD - 1
   {
-    const int64_t fe = vae_frame_elems(h->nout.c, x.H[3], x.W[3]);
     bf16_t* po[VAE_MAXF];
-    for (int j = 0; j < nD; ++j) po[j] = h->nout.slot(h->nout.hist + j, fe);
-    norm_launch(x, pd, po, nD, b, 3, h->g_out);
+    ring_slots(x, h->nout, 3, nD, po);
+    if (!normed) norm_launch(x, pd, po, nD, b, 3, h->g_out);
     VaeConvArgs a{};
     ring_inputs(x, h->nout, 3, nD, a);
     a.video = video;
