@@ -252,6 +252,29 @@ void run_ops() {
   expect(wan_op_attention_noalloc(q.t.data, 3 * D, (char*)q.t.data + 2 * D, 3 * D, vt.t.data, ldv, o.t.data, D, 4200,
                                   L, L, (int)nh, nullptr),
          WAN_ERR_UNSUPPORTED, "attention noalloc too large");
+  // GEMM with a workspace: 36 x 17 tiles of 256, 100 in the last round -> the stream-K chunks and fix-up
+  {
+    const int64_t M = 9000, N = 4104, K = 256;
+    Tensor x({M, K}, WAN_BF16), w({N, K}, WAN_BF16), bias({N}), ob({M, N}, WAN_BF16), of({M, N}), tab({N}),
+        src({(M + 99) / 100, N});
+    const int64_t wsb = wan_op_gemm_workspace_bytes();
+    Tensor ws({wsb / 4});
+    for (int epi = 0; epi <= 4; ++epi) {
+      void* out = epi < 2 ? ob.t.data : of.t.data;
+      expect(wan_op_gemm_ws(x.t.data, K, w.t.data, K, (const float*)bias.t.data, M, N, K, epi, out, N,
+                            (const float*)tab.t.data, (const float*)src.t.data, N, 100, ws.t.data, wsb, nullptr),
+             WAN_OK, "gemm_ws");
+    }
+    expect(wan_op_gemm_ws(x.t.data, K, w.t.data, K, (const float*)bias.t.data, M, N, K, 0, ob.t.data, N, nullptr,
+                          nullptr, 0, 1, ws.t.data, wsb - 16, nullptr),
+           WAN_ERR_INVALID_ARG, "gemm_ws short workspace");
+    expect(wan_op_gemm_ws(x.t.data, K, w.t.data, K, (const float*)bias.t.data, M, N, K, 0, ob.t.data, N, nullptr,
+                          nullptr, 0, 1, (char*)ws.t.data + 4, wsb - 16, nullptr),
+           WAN_ERR_INVALID_ARG, "gemm_ws misaligned workspace");
+    expect(wan_op_gemm_ws(x.t.data, K, w.t.data, K, (const float*)bias.t.data, M, N, 100, 0, ob.t.data, N, nullptr,
+                          nullptr, 0, 1, ws.t.data, wsb, nullptr),
+           WAN_ERR_SHAPE, "gemm_ws K not a multiple of 64");
+  }
 }
 
 }  // namespace

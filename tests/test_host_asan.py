@@ -4,7 +4,8 @@ AddressSanitizer and UndefinedBehaviorSanitizer, the HIP runtime replaced by tes
 tests/host_asan/driver.cpp drives the C ABI: weight matching (missing, duplicate, mis-shaped, mis-typed
 weights), workspace planning and the whole launch sequence of the DiT forward (per-token timesteps, the
 image branch, the denoising step, attention timing) and of the VAE decode (1, 2, 6 and 9 latent frames,
-batch 2, a size change, frame rings), the argument checks, and the allocation-free attention.  Leaks and
+batch 2, a size change, frame rings), the argument checks, the allocation-free attention and the GEMM with a
+workspace (its stream-K tail).  Leaks and
 memory errors fail the run; so does a launch with an impossible shape.
 """
 import os
