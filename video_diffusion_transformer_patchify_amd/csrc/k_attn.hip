@@ -24,18 +24,23 @@
 //   * Keys are processed in 32-key sub-tiles j, software pipelined: the MFMAs of S(j+1) are issued
 //     together with the exp / row-sum / bf16 packing of S(j), then the PV MFMAs of sub-tile j together
 //     with the copy of S(j+1) out of the accumulator registers, so matrix and vector work of one wave
-//     overlap.
+//     overlap.  The K and Vt fragments of a step are read from LDS during the step before it.
 //   * Softmax in base 2: Q enters the score MFMAs multiplied by log2(e)/sqrt(128), so S is already in
 //     log2 units and a probability is one exp2 of an accumulator value, with no offset at all: the row's
 //     scores are not reduced to a running max while they stay in a safe range (any common offset of
-//     numerator and denominator cancels in the final division).  Each sub-tile's per-lane probability
-//     sum is checked against 2^64 (no overflow anywhere after), and the first sub-tile's row max against
-//     -60 (the largest probability stays a normal float); the check is branch-free, so the loop stays
-//     one block.  A wave whose rows leave that range drops its results and marks its unit; the exact
+//     numerator and denominator cancels in the final division).  Each lane's total probability sum is
+//     checked against 2^64 after the last sub-tile (every probability is at most that sum, so nothing
+//     overflowed on the way; an infinite or NaN probability fails the check too), and the first
+//     sub-tile's row max against -60 (the largest probability stays a normal float); both checks are
+//     branch-free, so the loop stays one block.  A wave whose rows leave that range drops its results
+//     and marks its unit; the exact
 //     kernel (same file, EXACT) then recomputes the marked units with the online softmax: a running
 //     max, raised only when a sub-tile's max passes it by more than 8 (the stale max keeps
 //     probabilities below 2^8), rescaling O and l when it is.
-//   * Row sums stay per lane half and are combined once at the end.
+//   * Row sums (offset-free kernel) run on the matrix cores: v_mfma_f32_4x4x4_16b_bf16 with an all-ones
+//     A operand adds each lane's own bf16 probabilities (the ones the PV MFMAs use) into an fp32
+//     accumulator, 8 small MFMAs per step in place of 32 vector adds; the two lane halves of a row are
+//     combined once at the end.  The exact kernel sums on the vector units (its sums are rescaled).
 //   * Only the last sub-tile can be partial; its scores are masked in a peeled copy of the loop body.
 #include <type_traits>
 
@@ -52,7 +57,7 @@ constexpr int QB = 4 * QWAVE;       // queries per workgroup
 constexpr int K_TILE_BYTES = KT * 256;     // 64 rows of 128 bf16
 constexpr int V_TILE_BYTES = 128 * KT * 2; // 128 rows of 64 bf16
 constexpr int TILE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
-constexpr float SUM_LIMIT = 18446744073709551616.0f;   // 2^64: largest per-lane sub-tile sum, offset-free
+constexpr float SUM_LIMIT = 18446744073709551616.0f;   // 2^64: largest per-lane row sum, offset-free
 constexpr float MAX_FLOOR = -60.0f;                    // smallest first-sub-tile row max, offset-free
 constexpr float RESCALE_LOG2 = 8.0f;                   // exact path: margin before the running max is raised
 constexpr int64_t ATTN_SPLIT_MAX = 256;   // workgroups of a key-split launch (default workspace size)
@@ -97,7 +102,12 @@ struct AttnState {
   float l_run[2];   // this lane half's sum of the row's probabilities
   float m[2];       // exponent offset of the probabilities (log2 units): 0 offset-free, else the running max
   bool bad;         // offset-free kernel, wave-uniform: a row left the safe range (the unit is redone exactly)
+  f32x4 lacc[2];    // offset-free kernel: this lane's sum of its bf16 probabilities (4 equal copies: the
+                    // 4x4x4 MFMA's output rows)
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));   // 4 bf16: an operand of the 4x4x4 bf16 MFMA
+__device__ __forceinline__ s16x4 as_s16x4(uint32_t a, uint32_t b) { return __builtin_bit_cast(s16x4, (u32x2){a, b}); }
 
 // S^T for sub-tile `sub` (0 or 1) of an LDS tile, both query blocks; each K fragment read once.
 __device__ __forceinline__ void scores(f32x16 (&s)[2], const u32x4 (&qf)[2][8], const char* lk, int sub, int l32,
@@ -149,19 +159,20 @@ __device__ __forceinline__ float row_max(const f32x16& s) {
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
-// P = exp2(s - m) as bf16 B-operand fragments (two 16-key steps per query block) and this lane's sums.
+// P = exp2(s - m) as bf16 B-operand fragments (two 16-key steps per query block); OFFSET (the exact
+// kernel) also this lane's fp32 sums.
 template <bool OFFSET>
 __device__ __forceinline__ void probs(const f32x16 (&s)[2], const float (&m)[2], u32x4 (&pf)[2][2], float (&ls)[2]) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float sum;
+    float sum = 0.f;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = __builtin_amdgcn_exp2f(OFFSET ? s[qb][8 * hh + e] - m[qb] : s[qb][8 * hh + e]);
-        sum = (hh == 0 && e == 0) ? p[e] : sum + p[e];
+        if constexpr (OFFSET) sum = (hh == 0 && e == 0) ? p[e] : sum + p[e];
       }
       u32x4 w;
       w.x = pack_bf16x2(p[0], p[1]); w.y = pack_bf16x2(p[2], p[3]);
@@ -193,21 +204,38 @@ __device__ __forceinline__ void raise_max(AttnState& st, const f32x16 (&s)[2]) {
   }
 }
 
-// Probabilities of the current sub-tile into pf; l accumulates their sums.  EXACT: against the running
-// max.  Otherwise offset-free; a lane sum above SUM_LIMIT marks the wave bad (its results are dropped and
-// its unit is recomputed by the exact kernel).
+// Probabilities of the current sub-tile into pf; their sums accumulate.  EXACT: against the running max,
+// summed into l_run.  Otherwise offset-free, summed into lacc by MFMAs (the 4x4x4 MFMA's output column is
+// the lane that holds the B operand's column, so with A = 1 each lane adds its own 4 values); finish_sums
+// checks the totals.
 template <bool EXACT>
 __device__ __forceinline__ void softmax_step(AttnState& st, const f32x16 (&s)[2], u32x4 (&pf)[2][2]) {
   float ls[2];
   if constexpr (EXACT) {
     raise_max(st, s);
     probs<true>(s, st.m, pf, ls);
+    st.l_run[0] += ls[0];
+    st.l_run[1] += ls[1];
   } else {
     probs<false>(s, st.m, pf, ls);
-    st.bad |= __any(!(fmaxf(ls[0], ls[1]) <= SUM_LIMIT));   // branch-free: the loop stays one block
+    const s16x4 ones = as_s16x4(0x3F803F80u, 0x3F803F80u);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        st.lacc[qb] =
+            __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones, as_s16x4(pf[qb][hh].x, pf[qb][hh].y), st.lacc[qb], 0, 0, 0);
+        st.lacc[qb] =
+            __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones, as_s16x4(pf[qb][hh].z, pf[qb][hh].w), st.lacc[qb], 0, 0, 0);
+      }
   }
-  st.l_run[0] += ls[0];
-  st.l_run[1] += ls[1];
+}
+// Offset-free kernel, after the last step: the lane sums into l_run, and the wave is marked bad if any
+// lane's sum left the safe range (above SUM_LIMIT, infinite or NaN).
+__device__ __forceinline__ void finish_sums(AttnState& st) {
+  st.l_run[0] = st.lacc[0][0];
+  st.l_run[1] = st.lacc[1][0];
+  st.bad |= __any(!(fmaxf(st.l_run[0], st.l_run[1]) <= SUM_LIMIT));
 }
 
 // O^T += V^T P^T for sub-tile `sub` of an LDS tile: A = Vt rows d = 32 dt + l32, keys 32 sub + 16 jj + 8 g.
@@ -224,6 +252,44 @@ __device__ __forceinline__ void pv(AttnState& st, const u32x4 (&pf)[2][2], const
       st.o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[1][jj]), st.o[1][dt], 0, 0, 0);
     }
   }
+}
+
+// K fragments of sub-tile `sub` of an LDS tile (rows in key_perm order), and the scores from them.
+__device__ __forceinline__ void read_k(u32x4 (&kf)[8], const char* lk, int sub, int l32, int g) {
+  const int row = KS * sub + key_perm(l32);
+  const char* kr = lk + row * 256;
+  const int sw = k_swz(row);
+#pragma unroll
+  for (int st = 0; st < 8; ++st) kf[st] = *(const u32x4*)(kr + (((2 * st + g) ^ sw) << 4));
+}
+__device__ __forceinline__ void scores_kf(f32x16 (&s)[2], const u32x4 (&qf)[2][8], const u32x4 (&kf)[8]) {
+  s[0] = (f32x16){};
+  s[1] = (f32x16){};
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[st]), as_bf16x8(qf[0][st]), s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[st]), as_bf16x8(qf[1][st]), s[1], 0, 0, 0);
+  }
+}
+// Vt fragments of sub-tile `sub` (the A operands of its PV MFMAs), and the PV MFMAs from them.
+__device__ __forceinline__ void read_v(u32x4 (&vf)[4][2], const char* lv, int sub, int l32, int g) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int row = 32 * dt + l32;
+    const char* vr = lv + row * 128;
+    const int sw = v_swz(row);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) vf[dt][jj] = *(const u32x4*)(vr + (((2 * (2 * sub + jj) + g) ^ sw) << 4));
+  }
+}
+__device__ __forceinline__ void pv_vf(AttnState& st, const u32x4 (&pf)[2][2], const u32x4 (&vf)[4][2]) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      st.o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[dt][jj]), as_bf16x8(pf[0][jj]), st.o[0][dt], 0, 0, 0);
+      st.o[1][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[dt][jj]), as_bf16x8(pf[1][jj]), st.o[1][dt], 0, 0, 0);
+    }
 }
 
 // SELF selects the instantiation only (self- and cross-attention then show up as separate kernels in
@@ -336,6 +402,7 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
     for (int i = 0; i < 4; ++i) st.o[qb][i] = (f32x16){};
     st.m[qb] = 0.f;
     st.l_run[qb] = 0.f;
+    st.lacc[qb] = (f32x4){};
   }
   st.bad = false;
   const int last_lim = (int)(Lkv - (int64_t)(n_sub - 1) * KS);   // valid keys in the last sub-tile
@@ -364,7 +431,19 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   wait_vm(4 * ((2 < n_tiles) + (3 < n_tiles) + (1 < n_tiles) + (2 < n_tiles)), std::false_type{});
   block_sync();
   f32x16 s_cur[2], s_next[2];
-  scores(s_next, qf, lds[0], 0, l32, g);
+  // Offset-free kernel: fragments are read one step ahead of their MFMAs, kf = K of the sub-tile whose
+  // scores the next step forms, vf = Vt of the sub-tile whose PV it runs (the barrier schedule below
+  // covers those reads too).  The exact kernel reads them where they are used (fewer live registers).
+  constexpr bool AHEAD = !EXACT;
+  u32x4 kf[8], vf[4][2];
+  if constexpr (AHEAD) {
+    read_k(kf, lds[0], 0, l32, g);
+    scores_kf(s_next, qf, kf);
+    if (n_sub > 1) read_k(kf, lds[0], 1, l32, g);
+    read_v(vf, lds[0] + K_TILE_BYTES, 0, l32, g);
+  } else {
+    scores(s_next, qf, lds[0], 0, l32, g);
+  }
   if (n_sub == 1 && last_lim < KS) mask_scores(s_next, g, last_lim);
   to_vgprs(s_next, s_cur);
   {
@@ -386,6 +465,9 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   // at the previous barrier or in the prologue: vmcnt(0)), then every wave's.  Every wave is also past
   // its last read of K(t) (first half of tile t) and of V(t-1) (second half of tile t-1), so the K
   // regions of tiles <= t and the V regions of tiles <= t-1 take K(t+4), K(t+5), V(t+3), V(t+4).
+  // Reading one step ahead stays inside that: the four steps then read K of sub-tiles 2t+3 .. 2t+6
+  // (tiles t+1 .. t+3) and Vt of sub-tiles 2t+2 .. 2t+5 (tiles t+1, t+2); K(t+3) went out at the
+  // previous barrier, so the vmcnt(0) + barrier here covers it as well.
   auto head = [&](int j, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int t = j >> 1, half = j & 1;
@@ -399,14 +481,24 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
       if (t + 3 < n_tiles) issue(t + 3, 1);
       if (t + 4 < n_tiles) issue(t + 4, 1);
     }
-    scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
+    if constexpr (AHEAD) {
+      scores_kf(s_next, qf, kf);
+      if constexpr (!LAST) read_k(kf, lds[((j + 2) >> 1) % NBUF], (j + 2) & 1, l32, g);
+    } else {
+      scores(s_next, qf, lds[((j + 1) >> 1) % NBUF], (j + 1) & 1, l32, g);
+    }
     if constexpr (LAST) {
       if (last_lim < KS) mask_scores(s_next, g, last_lim);
     }
   };
   // PV of sub-tile j; the next sub-tile's scores become current
   auto tail = [&](int j, const u32x4 (&pf)[2][2]) {
-    pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
+    if constexpr (AHEAD) {
+      pv_vf(st, pf, vf);
+      read_v(vf, lds[((j + 1) >> 1) % NBUF] + K_TILE_BYTES, (j + 1) & 1, l32, g);
+    } else {
+      pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
+    }
     to_vgprs(s_next, s_cur);
   };
   int j = 0;
@@ -427,11 +519,13 @@ __global__ __launch_bounds__(256, 1) void k_flash_attn(AttnArgs a) {
   {
     u32x4 pf[2][2];
     softmax_step<EXACT>(st, s_cur, pf);
-    pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
+    if constexpr (AHEAD) pv_vf(st, pf, vf);
+    else pv(st, pf, lds[(j >> 1) % NBUF] + K_TILE_BYTES, j & 1, l32, g);
   }
 
   // ---- normalise and store: o[qb][dt] element r holds d = 32 dt + 8 (r/4) + 4 g + r%4 of query qi[qb]
   if constexpr (!EXACT) {
+    finish_sums(st);
     if (lane == 0) a.flags[4 * (int64_t)wg + wave] = st.bad ? 1u : 0u;
     if (st.bad) return;
   } else {
@@ -524,6 +618,7 @@ __device__ __forceinline__ void resident_pass(AttnState& st, const u32x4 (&qf)[2
     for (int i = 0; i < 4; ++i) st.o[qb][i] = (f32x16){};
     st.m[qb] = 0.f;
     st.l_run[qb] = 0.f;
+    st.lacc[qb] = (f32x4){};
   }
   st.bad = false;
   f32x16 s_cur[2], s_next[2];
@@ -561,6 +656,7 @@ __device__ __forceinline__ void resident_pass(AttnState& st, const u32x4 (&qf)[2
     softmax_step<EXACT>(st, s_cur, pf);
     pv(st, pf, lds[j >> 1] + K_TILE_BYTES, j & 1, l32, g);
   }
+  if constexpr (!EXACT) finish_sums(st);
 }
 
 constexpr int OSTAGE_BYTES = 32 * 256;   // one wave's 32 output rows of 128 bf16
