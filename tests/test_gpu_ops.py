@@ -217,6 +217,26 @@ def test_gemm_stream_k_tail(G, M, N, K, epi):
     assert G.max_abs(got, ref) < 1e-4 * max(1.0, np.abs(ref).max())
 
 
+def test_gemm_ws_reused_across_calls(G):
+    """One workspace, two calls in a row on one stream: a stream-K shape, then a smaller one whose tail
+    takes fewer chunks; each matches the plain entry point to fp32 summation order."""
+    import torch
+
+    ws = torch.empty(G.B.gemm_workspace_bytes() // 4, dtype=torch.float32, device="cuda")
+    for M, N, K in [(27280, 3072, 3072), (9000, 4104, 256)]:
+        G.note(f"gemm_ws reuse M={M} N={N} K={K}")
+        x, _ = G.bf16_dev((M, K), f"gx{M}{K}")
+        w, _ = G.bf16_dev((N, K), f"gw{N}{K}", 0.02)
+        bias = G.to_device(G.draw_normal(0, f"gb{N}", (N,), "f32", 0.02))
+        out = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        plain = torch.empty_like(out)
+        G.B.op_gemm(x, w, bias, 2, out, workspace=ws)
+        G.B.op_gemm(x, w, bias, 2, plain)
+        G.sync()
+        assert G.rel_l2(G.to_f64(out), G.to_f64(plain)) < 1e-6
+        assert G.max_abs(G.to_f64(out), G.to_f64(plain)) < 1e-5 * max(1.0, float(plain.abs().max()))
+
+
 def test_gemm_ws_rejects_bad_workspace(G):
     import torch
 
